@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of libgemm on one MI355X.
+
+One step = one GEMM call of the workload (the whole hot path: tile mapping, pipelined
+global->LDS slabs, fragment loads, MFMA / FMA math, epilogue), with inputs resident in
+HBM.  Default workload: bf16 GEMM M = N = K = 8192, A row-major and B column-major
+(both K-contiguous), bf16 output, alpha = 1, beta = 0 -- the shape the metric's
+70 %-of-peak target is stated on.  Prints ONE JSON line.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1..c5] [--nstage S]
+                  [--no-sweep] [--no-cpu-baseline]
+
+The other four workloads are reported under "workloads" (TFLOP/s and fraction of the
+dense peak of their arithmetic), with nStage sweeps for the pipelining comparison.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import glob
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+import torch  # noqa: E402
+
+from tiled_stage_software_amd import inputs, libgemm as lg  # noqa: E402
+
+METRIC = "GEMM TFLOP/s (2MNK/t) per shape at 1 MI355X; % of fp32/bf16 dense peak"
+PEAK = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}      # TFLOP/s, MI355X published dense figures
+BOUND = {"bf16": "mfma", "f16": "mfma", "f32": "alu"}
+DT_CODE = {"f32": lg.GEMM_F32, "bf16": lg.GEMM_BF16, "f16": lg.GEMM_F16}
+WORKLOAD_NAME = {
+    "c1": "fp32 GEMM 256x256x256 NN (row-major A, B), alpha=1 beta=0",
+    "c2": "fp32 GEMM 4096x4096x4096 NN (row-major A, B), 128x64 tile, alpha=1 beta=0",
+    "c3": "bf16 GEMM 8192x8192x8192 NT (A row-major, B column-major), fp32 accumulate, bf16 out",
+    "c4": "f16 GEMM M=16384 N=14336 K=4096 NT, fp32 accumulate, f16 out",
+    "c5": "bf16 GEMM M=4000 N=3000 K=2049 NN, fp32 C, alpha=0.5 beta=1",
+}
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "tiled_stage_software_amd", "csrc", "*"))):
+        with open(f, "rb") as fh:
+            h.update(os.path.basename(f).encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+class Workload:
+    def __init__(self, name: str, dev):
+        self.name = name
+        self.cfg = inputs.CONFIGS[name]
+        self.p = inputs.make_problem(self.cfg)
+        p = self.p
+        self.A = p.A.storage.to(dev)
+        self.B = p.B.storage.to(dev)
+        out_dt = inputs.DTYPES[p.out]
+        self.C0 = p.C0.storage.to(dev) if p.C0 is not None else None
+        self.C = torch.zeros(p.M * p.N, dtype=out_dt, device=dev) if self.C0 is None else self.C0.clone()
+        self.flops = 2.0 * p.M * p.N * p.K
+        self.stream = torch.cuda.current_stream(dev)
+
+    def plan(self, nstage=0, kernel=0, tile=0):
+        p = self.p
+        o = lg.GemmOpts(nstage, kernel, tile, 0) if (nstage or kernel or tile) else None
+        s, pl = lg.gemm_plan(DT_CODE[p.dtype], DT_CODE[p.out], p.A.layout, p.B.layout, p.M, p.N, p.K, p.alpha,
+                             self.A.data_ptr(), p.A.ld, self.B.data_ptr(), p.B.ld, p.beta, self.C.data_ptr(), p.N, o)
+        lg.check(s)
+        return pl
+
+    def step(self, nstage=0, kernel=0, tile=0):
+        p = self.p
+        s = lg.gemm_operands(p.dtype, p.out, p.A.layout, p.B.layout, p.M, p.N, p.K, p.alpha,
+                             self.A.data_ptr(), p.A.ld, self.B.data_ptr(), p.B.ld, p.beta, self.C.data_ptr(), p.N,
+                             self.stream.cuda_stream, nstage=nstage, kernel=kernel, tile=tile)
+        if s != lg.GEMM_OK:
+            raise lg.GemmError(s, lg.gemm_last_error())
+
+    def reset_c(self):
+        if self.C0 is not None:
+            self.C.copy_(self.C0)
+
+    def time(self, steps: int, warmup: int, **opts):
+        """Average ms per launch over `steps` back-to-back launches (HIP events on the
+        launch stream).  With beta != 0 C accumulates across steps; the work per step is
+        unchanged."""
+        for _ in range(warmup):
+            self.step(**opts)
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(steps):
+            self.step(**opts)
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+
+def cpu_baseline(w: Workload, target_s: float, nthreads: int):
+    """Time the oracle (as it stands) on a bounded row sample of the workload on the host
+    cores, and check the device result on the same rows."""
+    from oracle import oracle
+    p = w.p
+    la, lb = p.A.layout == inputs.COL, p.B.layout == inputs.COL
+    # probe with a few rows, then size the sample to ~target_s seconds
+    probe_rows = [0, p.M - 1]
+    t0 = time.perf_counter()
+    oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
+                    None if p.C0 is None else p.C0.storage, p.N, rows=probe_rows, nthreads=nthreads)
+    dt = max(time.perf_counter() - t0, 1e-4)
+    per_row = dt / len(probe_rows)
+    threads = oracle.max_threads(nthreads)
+    n = int(target_s / per_row * min(threads, 8) / 2)
+    n = max(threads, min(p.M, n))
+    rows = sorted(set(np.linspace(0, p.M - 1, n).astype(np.int64).tolist()))
+    t0 = time.perf_counter()
+    ref = oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
+                          None if p.C0 is None else p.C0.storage, p.N, rows=rows, nthreads=nthreads)
+    el = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * p.N * p.K
+    # device check on the same rows (fresh result, C restored first when beta != 0)
+    w.reset_c()
+    w.step()
+    torch.cuda.synchronize()
+    got = w.C.view(p.M, p.N)[torch.tensor(rows, device=w.C.device)].double().cpu().numpy()
+    err = oracle.normalized_error(got, ref, p.K, p.A.logical().abs().max().item(), p.B.logical().abs().max().item())
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(rows)} of {p.M} rows x all {p.N} columns (fp64 oracle, {el:.1f} s)",
+            "seconds": el, "err_vs_device": err}
+
+
+def traffic_for(name: str, src_hash: str, launch_flops: float):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
+    on the current kernel sources (else null)."""
+    f = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
+    if not os.path.exists(f):
+        return None
+    with open(f) as fh:
+        d = json.load(fh)
+    if d.get("kernel_source_hash") != src_hash:
+        return None
+    return d.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="c3", choices=sorted(inputs.CONFIGS))
+    ap.add_argument("--nstage", type=int, default=0)
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--kernel", type=int, default=0)
+    ap.add_argument("--no-sweep", action="store_true", help="skip the other workloads and nStage sweeps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--only", action="store_true", help="time only the headline launches (for profiling)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
+              "a GEMM shards into independent output tiles, see DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    lg.load()
+    src_hash = kernel_source_hash()
+
+    w = Workload(args.config, dev)
+    opts = dict(nstage=args.nstage, kernel=args.kernel, tile=args.tile)
+    plan = w.plan(**opts)
+    ms = w.time(args.steps, args.warmup, **opts)
+    value = w.flops / (ms * 1e-3) / 1e12
+    dt = w.p.dtype
+    rec = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": dt, "data": "synthetic (seeded)",
+        "config": {"workload": WORKLOAD_NAME[args.config], "M": w.p.M, "N": w.p.N, "K": w.p.K,
+                   "A": "row" if w.p.A.layout == 0 else "col", "B": "row" if w.p.B.layout == 0 else "col",
+                   "out": w.p.out, "alpha": w.p.alpha, "beta": w.p.beta, "kernel": plan.as_dict()},
+        "frac_of_peak": round(value / PEAK[dt], 4),
+    }
+    rec["roofline"] = {"bound": BOUND[dt], "achieved": round(value, 2), "peak": PEAK[dt], "unit": "TFLOP/s",
+                       "frac": round(value / PEAK[dt], 4),
+                       "traffic": traffic_for(args.config, src_hash, w.flops)}
+    if args.only:
+        print(json.dumps(rec), flush=True)
+        return
+
+    if not args.no_sweep:
+        sweep = {}
+        for name in ("c1", "c2", "c3", "c4", "c5"):
+            ww = w if name == args.config else Workload(name, dev)
+            pl = ww.plan()
+            reps = 2000 if name == "c1" else 30
+            entry = {"workload": WORKLOAD_NAME[name], "kernel": pl.as_dict()}
+            t = ww.time(reps, 5)
+            entry["ms"] = round(t, 5)
+            entry["tflops"] = round(ww.flops / (t * 1e-3) / 1e12, 2)
+            entry["frac_of_peak"] = round(entry["tflops"] / PEAK[ww.p.dtype], 4)
+            # pipelining comparison on the ring kernel of the default tile
+            if pl.kernel in (lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING):
+                stages = {}
+                for S in range(1, 5):
+                    q = lg.GemmOpts(S, pl.kernel, pl.tile, 0)
+                    s, _ = lg.gemm_plan(DT_CODE[ww.p.dtype], DT_CODE[ww.p.out], ww.p.A.layout, ww.p.B.layout,
+                                        ww.p.M, ww.p.N, ww.p.K, ww.p.alpha, ww.A.data_ptr(), ww.p.A.ld,
+                                        ww.B.data_ptr(), ww.p.B.ld, ww.p.beta, ww.C.data_ptr(), ww.p.N, q)
+                    if s != lg.GEMM_OK:
+                        continue
+                    ts = ww.time(reps, 5, nstage=S, kernel=pl.kernel, tile=pl.tile)
+                    stages[str(S)] = {"ms": round(ts, 5), "tflops": round(ww.flops / (ts * 1e-3) / 1e12, 2)}
+                entry["nstage_sweep"] = stages
+            sweep[name] = entry
+            if ww is not w:
+                del ww
+                torch.cuda.empty_cache()
+        rec["workloads"] = sweep
+
+    if not args.no_cpu_baseline:
+        w.reset_c()
+        rec["cpu_baseline"] = cpu_baseline(w, args.cpu_seconds, int(os.environ.get("OMP_NUM_THREADS", "0") or 0))
+    rec["kernel_source_hash"] = src_hash
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,172 @@
+/*
+ * libgemm.h -- C ABI of the tiled, software-pipelined GEMM library for AMD MI355X (gfx950).
+ *
+ * Operation (every entry point):   C = alpha * A * B + beta * C
+ *
+ *   The accumulation C += A * B, looped over the K dimension one tile ("K-slab") at a
+ *   time with hierarchical block / wave / thread tiles, is sections 1-4 of the page
+ *   "CUTLASS-Cute 初步(6)：CUDA GEMM 计算优化、Multi-Stage 与软流水"; alpha and beta
+ *   follow the BLAS convention.  While one K-slab is multiplied out of LDS, the next
+ *   slab(s) stream from HBM into other buffers of an nStage LDS ring ("Software
+ *   Pipelining and Double Buffering", sections "Double buffering with shared memory"
+ *   and "Multi-stage pipelines"; the N-stage ring of "Matrix multiplication").
+ *
+ * Storage (BLAS index form), all leading dimensions in ELEMENTS:
+ *   A (M x K): GEMM_ROW_MAJOR -> A[m*lda + k],  GEMM_COL_MAJOR -> A[k*lda + m]
+ *   B (K x N): GEMM_ROW_MAJOR -> B[k*ldb + n],  GEMM_COL_MAJOR -> B[n*ldb + k]
+ *   C (M x N): always row-major, C[m*ldc + n]
+ *   ("NT" = A row-major, B column-major: both operands K-contiguous.)
+ *
+ * Arithmetic: products of the inputs are accumulated in fp32.  FP32 inputs use one
+ *   fused multiply-add chain per output in ascending k (VALU path).  bf16 / f16 inputs
+ *   use the matrix cores (v_mfma_f32_32x32x16_{bf16,f16}).  The epilogue computes, in
+ *   fp32, alpha*acc when beta == 0 (C is then never read, so NaN in C does not leak)
+ *   and fmaf(alpha, acc, beta*C) otherwise, then rounds to the C type with
+ *   round-to-nearest-even.  f16 subnormal inputs are not flushed.  The k order seen by
+ *   every accumulator does not depend on nstage, so results are bit-identical across
+ *   stage counts and across runs.
+ *
+ * Pointers: A, B and C are DEVICE pointers owned by the caller.  The library allocates
+ *   nothing, keeps no pointer after returning and holds no mutable global state apart
+ *   from a thread-local error string; calls are reentrant.  C must not overlap A or B
+ *   (not checked).  Misaligned pointers or leading dimensions are never an error: they
+ *   select a slower load path.
+ *
+ * Streams: the work is enqueued on `stream` (NULL = the null stream) and the call
+ *   returns without synchronising.  Faults during execution surface at the caller's
+ *   next synchronisation.
+ *
+ * Errors: argument checks run before anything is launched; on a non-OK status nothing
+ *   was enqueued and gemm_last_error() describes the problem.
+ *   GEMM_ERR_INVALID_ARG -- negative size, leading dimension below the minimum
+ *       (lda >= (la == ROW ? K : M), ldb >= (lb == ROW ? N : K), ldc >= N; each >= 1),
+ *       NULL pointer where it would be dereferenced (A and B when alpha != 0 and K > 0;
+ *       C when M*N > 0), bad enum value, a C type that the entry point does not offer.
+ *   GEMM_ERR_UNSUPPORTED -- gemm_opts_t asks for a kernel / stage count / tile that
+ *       cannot run this problem (e.g. the direct-to-LDS ring on a misaligned operand,
+ *       or a ring that exceeds the 160 KiB of LDS).
+ *   GEMM_ERR_HIP -- the HIP runtime refused the launch (message in gemm_last_error()).
+ *   Quick returns (BLAS): M == 0 or N == 0 -> OK, nothing launched.  K == 0 or
+ *   alpha == 0 -> C = beta*C (beta == 0 writes zeros without reading C).
+ */
+#ifndef LIBGEMM_H
+#define LIBGEMM_H
+
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_INVALID_ARG = 1,
+    GEMM_ERR_UNSUPPORTED = 2,
+    GEMM_ERR_HIP = 3
+} gemm_status_t;
+
+typedef enum gemm_layout { GEMM_ROW_MAJOR = 0, GEMM_COL_MAJOR = 1 } gemm_layout_t;
+
+typedef enum gemm_dtype { GEMM_F32 = 0, GEMM_BF16 = 1, GEMM_F16 = 2 } gemm_dtype_t;
+
+/* Kernel families (gemm_opts_t.kernel). */
+typedef enum gemm_kernel {
+    GEMM_KERNEL_AUTO = 0,
+    GEMM_KERNEL_VALU_RING = 1,   /* fp32 VALU, direct global->LDS nStage ring (A row-major, B row-major) */
+    GEMM_KERNEL_VALU_STAGED = 2, /* fp32 VALU, loads staged through registers, any layout / alignment */
+    GEMM_KERNEL_MFMA_RING = 3,   /* bf16/f16 MFMA, direct global->LDS nStage ring (A and B K-contiguous) */
+    GEMM_KERNEL_MFMA_STAGED = 4, /* bf16/f16 MFMA, loads staged through registers, any layout / alignment */
+    GEMM_KERNEL_SCALE = 5        /* C = beta*C only (K == 0 or alpha == 0) */
+} gemm_kernel_t;
+
+#define GEMM_MAX_NSTAGE 5
+
+/* Optional knobs for tests and benchmarks.  All-zero = library default. */
+typedef struct gemm_opts {
+    int nstage; /* 0 = default, else 1..GEMM_MAX_NSTAGE: number of LDS slab buffers.
+                   1 = single buffer (load; barrier; compute; barrier), 2 = double buffer,
+                   n = n-1 slabs in flight while one is computed. Staged kernels: 1 or 2. */
+    int kernel; /* gemm_kernel_t; 0 = automatic choice */
+    int tile;   /* 0 = default tile of the kernel family, else a tile id (gemm_plan_t.tile) */
+    int flags;  /* bit 0: disable the XCD-aware workgroup order (plain row-major tile order);
+                   other bits must be 0 */
+} gemm_opts_t;
+
+#define GEMM_FLAG_NO_XCD_REMAP 1
+
+/* What a call would launch (filled by gemm_plan; no GPU needed). */
+typedef struct gemm_plan {
+    int kernel;        /* gemm_kernel_t actually chosen */
+    int nstage;
+    int tile;          /* tile id within the family */
+    int bm, bn, bk;    /* block tile (C rows, C cols, K-slab depth) */
+    int threads;       /* threads per workgroup */
+    int lds_bytes;     /* LDS per workgroup */
+    int64_t grid;      /* workgroups launched (0 if nothing is launched) */
+} gemm_plan_t;
+
+/* fp32 A, B, C. */
+gemm_status_t gemm_f32(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float beta, float* C, int64_t ldc, hipStream_t stream);
+
+/* bf16 A, B (raw 16-bit words); C is bf16 (c_type = GEMM_BF16) or fp32 (GEMM_F32). */
+gemm_status_t gemm_bf16(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                        float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream);
+
+/* f16 A, B; C is f16 (c_type = GEMM_F16) or fp32 (GEMM_F32). */
+gemm_status_t gemm_f16(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                       float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream);
+
+/* Same, with explicit knobs (opts may be NULL = defaults). */
+gemm_status_t gemm_f32_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                          float alpha, const float* A, int64_t lda, const float* B, int64_t ldb,
+                          float beta, float* C, int64_t ldc, hipStream_t stream,
+                          const gemm_opts_t* opts);
+gemm_status_t gemm_bf16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                           float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                           const gemm_opts_t* opts);
+gemm_status_t gemm_f16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                          float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                          float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                          const gemm_opts_t* opts);
+
+/* Validate and choose exactly as the corresponding gemm_*_ex call would, without
+ * launching anything (host only; pointers are inspected for NULL and alignment, never
+ * dereferenced).  in_type: GEMM_F32 / GEMM_BF16 / GEMM_F16.  Returns the status the
+ * call would return before launching; *plan is filled when it returns GEMM_OK. */
+gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb,
+                        int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
+                        const gemm_opts_t* opts, gemm_plan_t* plan);
+
+/* The K-loop protocol of a kernel family, as the event list its mainloop executes
+ * (host only, for checking the pipeline on the CPU).  Each event is 4 ints
+ * {type, slab, slot, arg}:
+ *   1 ISSUE    slab -> slot: asynchronous global->LDS copy of K-slab `slab` into ring
+ *              slot `slot` (staged kernels: slot == -1, a global->register load)
+ *   2 WAIT     arg = number of the newest issued slabs that may still be in flight
+ *   3 BARRIER  all waves of the workgroup
+ *   4 COMPUTE  read ring slot `slot`, holding slab `slab` (arg = k-step within the slab,
+ *              or -1 for a whole slab)
+ *   5 WRITE    staged kernels: registers of slab `slab` -> ring slot `slot`
+ *   6 WAIT_LDS the wave's own LDS reads and writes have completed
+ * kernel: GEMM_KERNEL_VALU_RING / MFMA_RING / VALU_STAGED / MFMA_STAGED; ksteps = k-steps
+ * per slab (ring kernels).  Returns the number of events (writes at most `capacity`
+ * of them), or -1 for bad arguments. */
+int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity);
+
+const char* gemm_status_string(gemm_status_t status);
+
+/* Thread-local description of the last non-OK status on this thread ("" if none). */
+const char* gemm_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBGEMM_H */

@@ -1,0 +1,161 @@
+"""C ABI checks that need no GPU: the library loads, exports what include/libgemm.h
+declares, rejects bad arguments before launching anything, and plans the kernel the
+problem calls for."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from tiled_stage_software_amd import libgemm as lg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "libgemm.h")
+
+ROW, COL = lg.GEMM_ROW_MAJOR, lg.GEMM_COL_MAJOR
+A16 = 0x10000   # fake, 16-byte aligned device addresses (never dereferenced by gemm_plan)
+B16 = 0x20000
+C16 = 0x30000
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(gemm_\w+)\s*\(", src, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    assert set(names) == set(lg.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", lg.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    lib = lg.load()
+    for n in declared_functions():
+        assert hasattr(lib, n)
+
+
+def test_status_strings():
+    assert lg.gemm_status_string(0) == "GEMM_OK"
+    assert lg.gemm_status_string(1) == "GEMM_ERR_INVALID_ARG"
+    assert lg.gemm_status_string(2) == "GEMM_ERR_UNSUPPORTED"
+    assert lg.gemm_status_string(3) == "GEMM_ERR_HIP"
+
+
+def plan(in_t, c_t, la, lb, M, N, K, alpha=1.0, A=A16, lda=None, B=B16, ldb=None, beta=0.0, C=C16, ldc=None,
+         **opts):
+    lda = lda if lda is not None else (K if la == ROW else M)
+    ldb = ldb if ldb is not None else (N if lb == ROW else K)
+    ldc = ldc if ldc is not None else N
+    o = lg.GemmOpts(opts.get("nstage", 0), opts.get("kernel", 0), opts.get("tile", 0), opts.get("flags", 0)) \
+        if opts else None
+    return lg.gemm_plan(in_t, c_t, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, o)
+
+
+F32, BF16, F16 = lg.GEMM_F32, lg.GEMM_BF16, lg.GEMM_F16
+
+
+@pytest.mark.parametrize("case,want", [
+    (dict(M=-1), lg.GEMM_ERR_INVALID_ARG),
+    (dict(N=-2), lg.GEMM_ERR_INVALID_ARG),
+    (dict(K=-3), lg.GEMM_ERR_INVALID_ARG),
+    (dict(lda=31), lg.GEMM_ERR_INVALID_ARG),        # row-major A needs lda >= K = 32
+    (dict(ldb=47), lg.GEMM_ERR_INVALID_ARG),        # row-major B needs ldb >= N = 48
+    (dict(ldc=47), lg.GEMM_ERR_INVALID_ARG),
+    (dict(A=0), lg.GEMM_ERR_INVALID_ARG),
+    (dict(B=0), lg.GEMM_ERR_INVALID_ARG),
+    (dict(C=0), lg.GEMM_ERR_INVALID_ARG),
+    (dict(la=7), lg.GEMM_ERR_INVALID_ARG),
+    (dict(nstage=6), lg.GEMM_ERR_UNSUPPORTED),
+    (dict(nstage=-1), lg.GEMM_ERR_UNSUPPORTED),
+    (dict(flags=4), lg.GEMM_ERR_INVALID_ARG),
+    (dict(kernel=lg.GEMM_KERNEL_MFMA_RING), lg.GEMM_ERR_UNSUPPORTED),   # fp32 input on the MFMA path
+    (dict(kernel=lg.GEMM_KERNEL_VALU_RING, A=A16 + 4), lg.GEMM_ERR_UNSUPPORTED),  # misaligned
+    (dict(kernel=lg.GEMM_KERNEL_VALU_STAGED, nstage=3), lg.GEMM_ERR_UNSUPPORTED),
+])
+def test_invalid_arguments(case, want):
+    args = dict(in_t=F32, c_t=F32, la=ROW, lb=ROW, M=40, N=48, K=32)
+    args.update(case)
+    s, _ = plan(**args)
+    assert s == want, (case, lg.gemm_status_string(s), lg.gemm_last_error())
+    assert lg.gemm_last_error() != ""
+
+
+def test_null_pointers_allowed_when_unused():
+    assert plan(F32, F32, ROW, ROW, 0, 8, 8, A=0, B=0, C=0)[0] == lg.GEMM_OK      # M == 0
+    assert plan(F32, F32, ROW, ROW, 8, 8, 0, A=0, B=0, lda=1)[0] == lg.GEMM_OK    # K == 0: scale only
+    assert plan(F32, F32, ROW, ROW, 8, 8, 8, alpha=0.0, A=0, B=0)[0] == lg.GEMM_OK
+
+
+def test_c_type_must_match_entry_point():
+    assert plan(BF16, F16, ROW, COL, 64, 64, 64)[0] == lg.GEMM_ERR_INVALID_ARG
+    assert plan(F16, BF16, ROW, COL, 64, 64, 64)[0] == lg.GEMM_ERR_INVALID_ARG
+    assert plan(F32, BF16, ROW, ROW, 64, 64, 64)[0] == lg.GEMM_ERR_INVALID_ARG
+    # the entry points themselves reject before touching the GPU
+    s = lg.gemm_bf16(ROW, COL, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, lg.GEMM_F16, 64, 0)
+    assert s == lg.GEMM_ERR_INVALID_ARG
+
+
+def test_quick_returns():
+    s, p = plan(BF16, BF16, ROW, COL, 0, 64, 64)
+    assert s == lg.GEMM_OK and p.grid == 0
+    s, p = plan(BF16, BF16, ROW, COL, 64, 0, 64, ldc=1)
+    assert s == lg.GEMM_OK and p.grid == 0
+    s, p = plan(BF16, BF16, ROW, COL, 64, 64, 0, lda=1, ldb=1)
+    assert s == lg.GEMM_OK and p.kernel == lg.GEMM_KERNEL_SCALE
+    s, p = plan(BF16, BF16, ROW, COL, 64, 64, 64, alpha=0.0)
+    assert s == lg.GEMM_OK and p.kernel == lg.GEMM_KERNEL_SCALE
+    # M == 0 through the entry point: nothing is launched, so this is safe without a GPU
+    assert lg.gemm_f32(ROW, ROW, 0, 5, 5, 1.0, 0, 5, 0, 5, 0.0, 0, 5, 0) == lg.GEMM_OK
+
+
+def test_plans_for_the_workloads():
+    # fp32 4096^3 NN -> direct ring, 128x64 tile
+    s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (128, 64)
+    assert p.grid == 32 * 64
+    # fp32 256^3 NN -> direct ring, small tile
+    s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (32, 32)
+    # bf16 8192^3 NT -> MFMA ring 256x256
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and (p.bm, p.bn) == (256, 256)
+    assert p.grid == 32 * 32 and p.lds_bytes <= 163840
+    # f16 MLP shape NT
+    s, p = plan(F16, F16, ROW, COL, 16384, 14336, 4096)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 56
+    # bf16 4000x3000x2049 NN, fp32 C: odd K and lda -> staged loader
+    s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED
+
+
+def test_ring_requirements_fall_back_to_staged():
+    # misaligned A pointer, odd leading dimension, K tail, small problem, wrong layout
+    for kw in (dict(A=A16 + 2), dict(lda=8201), dict(K=8190, lda=8192, ldb=8192), dict(M=100),
+               dict(la=COL, lda=8192)):
+        args = dict(in_t=BF16, c_t=BF16, la=ROW, lb=COL, M=8192, N=8192, K=8192)
+        args.update(kw)
+        s, p = plan(**args)
+        assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED, kw
+
+
+def test_lds_budget():
+    # 256x256x32 tile: 32 KiB per slot; 4 slots fit, 5 exactly fill 160 KiB but are not built
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=2, nstage=4)
+    assert s == 0 and p.lds_bytes == 4 * 32768
+    s, _ = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=1, nstage=3)
+    assert s == lg.GEMM_ERR_UNSUPPORTED       # 3 x 64 KiB > 160 KiB
+    s, _ = plan(F32, F32, ROW, ROW, 512, 512, 512, kernel=lg.GEMM_KERNEL_VALU_RING, tile=1, nstage=5)
+    assert s == lg.GEMM_ERR_UNSUPPORTED
+
+
+def test_forced_kernels_and_stages():
+    for S in (1, 2, 3, 4):
+        s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, kernel=lg.GEMM_KERNEL_VALU_RING, nstage=S)
+        assert s == 0 and p.nstage == S and p.lds_bytes == S * (128 * 16 + 16 * 64) * 4
+    s, p = plan(F32, F32, COL, COL, 100, 70, 33, kernel=lg.GEMM_KERNEL_VALU_STAGED, nstage=1)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_STAGED and p.nstage == 1

@@ -1,0 +1,297 @@
+// kernels_mfma.hip -- bf16 / f16 GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16).
+//
+// Hierarchy (sections 1-3 of "CUTLASS-Cute 初步(6)：CUDA GEMM 计算优化、Multi-Stage 与软流水"):
+//   workgroup tile BM x BN of C, looped over K in slabs of BK;
+//   WM x WN waves, each owning a disjoint (BM/WM) x (BN/WN) block of accumulators;
+//   per wave and per 16-deep k-step, (BM/WM/32) A fragments and (BN/WN/32) B fragments
+//   are read from LDS and combined by 32x32x16 MFMAs -- waves in one row of the tile
+//   read the same A fragments, waves in one column the same B fragments.
+//
+// Operand fragments (one 16-byte LDS read per lane): lane l holds 8 consecutive k of
+// row (l mod 32) of the 32-row block, k-chunk l/32 of the k-step.  The MFMA is fed
+// (B fragment, A fragment), so the 32x32 result it returns is C transposed: lane l,
+// register 4g+j holds C[m = l mod 32][n = 8g + 4*(l/32) + j], i.e. 4 consecutive columns
+// per lane and register group, which the epilogue stores as one vector.
+#include "common.hpp"
+#include "loaders.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+
+template <typename T>
+struct Mfma;
+template <>
+struct Mfma<__bf16> {
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<_Float16> {
+    typedef f16x8 frag;
+    static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+
+// Shared compute state: accumulators and double-buffered fragments of one wave.
+template <typename T, int BM, int BN, int BK, int WM, int WN>
+struct MfmaCompute {
+    static constexpr int ROWB = BK * 2;
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int WTM = BM / WM, WTN = BN / WN;
+    static constexpr int TM = WTM / 32, TN = WTN / 32;
+    static constexpr int KS = BK / 16;
+    static constexpr int A_BYTES = BM * ROWB;
+    static constexpr int B_BYTES = BN * ROWB;
+    static constexpr int STAGE = A_BYTES + B_BYTES;
+    static_assert(BK % 32 == 0, "two 16-deep k-steps per slab at least");
+    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is made of 32x32 blocks");
+
+    typedef typename Mfma<T>::frag frag_t;
+    f32x16 acc[TM][TN];
+    frag_t fa[2][TM];
+    frag_t fb[2][TN];
+    uint32_t a_off[KS];  // per lane LDS byte offsets within a stage (wave tile row 0)
+    uint32_t b_off[KS];
+    LDS_AS char* smem;
+
+    __device__ __forceinline__ void init(LDS_AS char* smem_) {
+        smem = smem_;
+        const int w = wave_id();
+        const int wm = w / WN, wn = w % WN;
+        const int lane = lane_id();
+        const int r = lane & 31;
+        const int hi = lane >> 5;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int c = 2 * ks + hi;
+            const int sw = c ^ swz<CPR>(r);  // wave-tile rows are multiples of 32: swz period 16
+            a_off[ks] = (uint32_t)((wm * WTM + r) * ROWB + (sw << 4));
+            b_off[ks] = (uint32_t)(A_BYTES + (wn * WTN + r) * ROWB + (sw << 4));
+        }
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+    }
+
+    template <int BUF>
+    __device__ __forceinline__ void frag(int slot, int ks) {
+        LDS_AS const char* st = smem + slot * STAGE;
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+            fa[BUF][i] = *reinterpret_cast<LDS_AS const frag_t*>(st + a_off[ks] + i * 32 * ROWB);
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+            fb[BUF][j] = *reinterpret_cast<LDS_AS const frag_t*>(st + b_off[ks] + j * 32 * ROWB);
+    }
+
+    template <int BUF>
+    __device__ __forceinline__ void math() {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(fb[BUF][j], fa[BUF][i], acc[i][j]);
+        // keep the k-step structure: the fragment loads issued before this math stay
+        // ahead of it and the next k-step's loads are not hoisted above it
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // Store the wave's accumulators.  (m0, n0): C coordinates of the tile computed;
+    // rows below m_keep / columns below n_keep belong to another tile (edge tiles are
+    // shifted inward to stay in bounds) and are not stored here.
+    template <int OUT>
+    __device__ __forceinline__ void epilogue(const GemmParams& p, int m0, int n0, int m_keep, int n_keep) {
+        const int w = wave_id();
+        const int wm = w / WN, wn = w % WN;
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const bool mok = m >= m_keep && m < p.M;
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int n = n0 + wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
+                    if (mok && n >= n_keep && n < p.N) {
+                        f32x4 v;
+                        v[0] = acc[i][j][4 * g + 0];
+                        v[1] = acc[i][j][4 * g + 1];
+                        v[2] = acc[i][j][4 * g + 2];
+                        v[3] = acc[i][j][4 * g + 3];
+                        store4<OUT>(p, m, n, v);
+                    }
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------- direct ring kernel
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S>
+struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN> C;
+    static constexpr int NW = WM * WN;
+    DirectLoader<BM, C::ROWB, NW, true> la;
+    DirectLoader<BN, C::ROWB, NW, true> lb;
+    static constexpr int L = DirectLoader<BM, C::ROWB, NW, true>::IPW + DirectLoader<BN, C::ROWB, NW, true>::IPW;
+
+    __device__ __forceinline__ void issue(int slab, int slot) {
+        LDS_AS char* st = this->smem + slot * C::STAGE;
+        la.issue(slab, st);
+        lb.issue(slab, st + C::A_BYTES);
+    }
+    template <int N>
+    __device__ __forceinline__ void wait_slabs() { wait_vm<N * L>(); }
+    __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    template <int BUF>
+    __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
+    occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, (BM / WM) * (BN / WN) > 64 * 64 ? 1 : 2))))
+void mfma_ring_kernel(const GemmParams p) {
+    typedef MfmaRingOps<T, BM, BN, BK, WM, WN, S> Ops;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    // Edge tiles are shifted inward so that every copy stays inside the matrix
+    // (the host guarantees M >= BM and N >= BN for this kernel).
+    const int m_keep = tm * BM, n_keep = tn * BN;
+    const int m0 = min(m_keep, p.M - BM);
+    const int n0 = min(n_keep, p.N - BN);
+    Ops ops;
+    ops.init((LDS_AS char*)(smem_raw));
+    ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
+    ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
+    gemm_sched::ring_mainloop<S, Ops::KS>(ops, p.K / BK);
+    ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+}
+
+// ---------------------------------------------------------------- staged kernel
+// AT / BT: the operand is contiguous across the LDS rows (A column-major, B row-major)
+// and is transposed on its way into the K-contiguous LDS tile.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, bool AT, bool BT>
+struct MfmaStagedOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN> C;
+    static constexpr int NT = WM * WN * 64;
+    StagedLoader<BM, BK, 2, NT, true, AT> la;
+    StagedLoader<BN, BK, 2, NT, true, BT> lb;
+
+    __device__ __forceinline__ void load(int slab) {
+        la.load(slab);
+        lb.load(slab);
+    }
+    __device__ __forceinline__ void write(int, int slot) {
+        LDS_AS char* st = this->smem + slot * C::STAGE;
+        la.write(st);
+        lb.write(st + C::A_BYTES);
+    }
+    __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    template <int BUF>
+    __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool AT, bool BT>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
+    occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, 2))))
+void mfma_staged_kernel(const GemmParams p) {
+    typedef MfmaStagedOps<T, BM, BN, BK, WM, WN, S, AT, BT> Ops;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    Ops ops;
+    ops.init((LDS_AS char*)(smem_raw));
+    // LDS rows of A are m (k along the row); of B, n.
+    ops.la.init(p.A, p.lda, m0, 0, p.M, p.K, p.a_vec != 0, false);
+    ops.lb.init(p.B, p.ldb, n0, 0, p.N, p.K, p.b_vec != 0, false);
+    gemm_sched::staged_mainloop<S, Ops::KS>(ops, (p.K + BK - 1) / BK);
+    ops.template epilogue<OUT>(p, m0, n0, m0, n0);
+}
+
+// ---------------------------------------------------------------- launch tables
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
+static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
+    const int grid = p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    return hipGetLastError();
+}
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
+static hipError_t launch_staged(const GemmParams& p, hipStream_t st) {
+    const dim3 grid(p.tiles_m * p.tiles_n), block(WM * WN * 64);
+    const bool at = p.a_col != 0, bt = p.b_col == 0;  // contiguous across the LDS rows
+    if (!at && !bt)
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, false>), grid, block, 0, st, p);
+    else if (!at && bt)
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, true>), grid, block, 0, st, p);
+    else if (at && !bt)
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, false>), grid, block, 0, st, p);
+    else
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, true>), grid, block, 0, st, p);
+    return hipGetLastError();
+}
+
+template <typename T, int OUT>
+static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
+    switch (tile) {
+        case 1:  // 256x256x64, 2x2 waves of 128x128
+            if (S == 1) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 1>(p, st);
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2>(p, st);
+            break;
+        case 2:  // 256x256x32, 2x2 waves of 128x128
+            if (S == 1) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 1>(p, st);
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 2>(p, st);
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 3>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 4>(p, st);
+            break;
+        case 3:  // 128x128x64, 2x2 waves of 64x64
+            if (S == 1) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 1>(p, st);
+            if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2>(p, st);
+            if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 4>(p, st);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename T, int OUT>
+static hipError_t staged_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
+    switch (tile) {
+        case 1:  // 128x128x32, 2x2 waves of 64x64
+            if (S == 1) return launch_staged<T, OUT, 128, 128, 32, 2, 2, 1>(p, st);
+            if (S == 2) return launch_staged<T, OUT, 128, 128, 32, 2, 2, 2>(p, st);
+            break;
+    }
+    return hipErrorInvalidValue;
+}
+
+// C is fp32 or the input type.
+hipError_t launch_mfma_ring(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st) {
+    if (in_type == DT_BF16)
+        return p.out_type == DT_F32 ? ring_dispatch<__bf16, DT_F32>(tile, nstage, p, st)
+                                    : ring_dispatch<__bf16, DT_BF16>(tile, nstage, p, st);
+    return p.out_type == DT_F32 ? ring_dispatch<_Float16, DT_F32>(tile, nstage, p, st)
+                                : ring_dispatch<_Float16, DT_F16>(tile, nstage, p, st);
+}
+hipError_t launch_mfma_staged(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st) {
+    if (in_type == DT_BF16)
+        return p.out_type == DT_F32 ? staged_dispatch<__bf16, DT_F32>(tile, nstage, p, st)
+                                    : staged_dispatch<__bf16, DT_BF16>(tile, nstage, p, st);
+    return p.out_type == DT_F32 ? staged_dispatch<_Float16, DT_F32>(tile, nstage, p, st)
+                                : staged_dispatch<_Float16, DT_F16>(tile, nstage, p, st);
+}
+
+}  // namespace gemm

@@ -1,0 +1,16 @@
+// launch.hpp -- host-side launchers of the kernel families (internal to the library).
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm {
+
+// Each launcher enqueues one kernel on `st` and returns hipGetLastError() (or
+// hipErrorInvalidValue for a tile / stage combination that is not instantiated).
+hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream_t st);
+hipError_t launch_valu_staged(int tile, int nstage, const GemmParams& p, hipStream_t st);
+hipError_t launch_mfma_ring(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st);
+hipError_t launch_mfma_staged(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st);
+hipError_t launch_scale(const GemmParams& p, hipStream_t st);
+
+}  // namespace gemm

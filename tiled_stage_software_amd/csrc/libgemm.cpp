@@ -1,0 +1,396 @@
+// libgemm.cpp -- the C ABI: argument checks, kernel choice and launch.
+//
+// Everything here runs on the host.  Arguments are checked before anything is
+// enqueued; the kernel family, tile and stage count are chosen from the layouts, the
+// alignment of the operands and the problem shape; the kernel is launched on the
+// caller's stream without synchronising.
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <vector>
+
+#include "libgemm.h"
+#include "launch.hpp"
+#include "schedule.hpp"
+
+namespace {
+
+using gemm::GemmParams;
+
+thread_local char g_err[512] = "";
+
+gemm_status_t fail(gemm_status_t s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+struct Tile {
+    int id, bm, bn, bk, threads, max_stage;
+    int stage_bytes;  // LDS per ring slot
+};
+
+// Instantiated tiles of each family (must match the launch tables of the kernels).
+const Tile kValuRing[] = {
+    {1, 128, 64, 16, 128, 4, (128 * 16 + 16 * 64) * 4},
+    {2, 64, 64, 16, 256, 4, (64 * 16 + 16 * 64) * 4},
+    {3, 32, 32, 16, 64, 4, (32 * 16 + 16 * 32) * 4},
+};
+const Tile kValuStaged[] = {
+    {1, 128, 64, 16, 128, 2, (128 * 16 + 16 * 64) * 4},
+    {3, 32, 32, 16, 64, 2, (32 * 16 + 16 * 32) * 4},
+};
+const Tile kMfmaRing[] = {
+    {1, 256, 256, 64, 256, 2, (256 + 256) * 64 * 2},
+    {2, 256, 256, 32, 256, 4, (256 + 256) * 32 * 2},
+    {3, 128, 128, 64, 256, 4, (128 + 128) * 64 * 2},
+};
+const Tile kMfmaStaged[] = {
+    {1, 128, 128, 32, 256, 2, (128 + 128) * 32 * 2},
+};
+
+constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
+
+template <size_t N>
+const Tile* find_tile(const Tile (&t)[N], int id) {
+    for (size_t i = 0; i < N; ++i)
+        if (t[i].id == id) return &t[i];
+    return nullptr;
+}
+
+struct Problem {
+    int in_type, c_type;
+    int la, lb;
+    int64_t M, N, K;
+    float alpha, beta;
+    const void* A;
+    const void* B;
+    const void* C;
+    int64_t lda, ldb, ldc;
+};
+
+int elem_size(int dt) { return dt == gemm::DT_F32 ? 4 : 2; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
+gemm_status_t validate(const Problem& q) {
+    if (q.la != GEMM_ROW_MAJOR && q.la != GEMM_COL_MAJOR) return fail(GEMM_ERR_INVALID_ARG, "la: bad layout %d", q.la);
+    if (q.lb != GEMM_ROW_MAJOR && q.lb != GEMM_COL_MAJOR) return fail(GEMM_ERR_INVALID_ARG, "lb: bad layout %d", q.lb);
+    if (q.M < 0 || q.N < 0 || q.K < 0)
+        return fail(GEMM_ERR_INVALID_ARG, "negative size (M=%lld N=%lld K=%lld)", (long long)q.M, (long long)q.N,
+                    (long long)q.K);
+    if (q.M > INT32_MAX || q.N > INT32_MAX || q.K > INT32_MAX)
+        return fail(GEMM_ERR_INVALID_ARG, "sizes must be below 2^31");
+    const int64_t min_lda = q.la == GEMM_ROW_MAJOR ? q.K : q.M;
+    const int64_t min_ldb = q.lb == GEMM_ROW_MAJOR ? q.N : q.K;
+    if (q.lda < 1 || q.lda < min_lda) return fail(GEMM_ERR_INVALID_ARG, "lda=%lld < %lld", (long long)q.lda, (long long)min_lda);
+    if (q.ldb < 1 || q.ldb < min_ldb) return fail(GEMM_ERR_INVALID_ARG, "ldb=%lld < %lld", (long long)q.ldb, (long long)min_ldb);
+    if (q.ldc < 1 || q.ldc < q.N) return fail(GEMM_ERR_INVALID_ARG, "ldc=%lld < N=%lld", (long long)q.ldc, (long long)q.N);
+    if (q.M > 0 && q.N > 0) {
+        if (!q.C) return fail(GEMM_ERR_INVALID_ARG, "C is NULL");
+        if (q.alpha != 0.0f && q.K > 0) {
+            if (!q.A) return fail(GEMM_ERR_INVALID_ARG, "A is NULL");
+            if (!q.B) return fail(GEMM_ERR_INVALID_ARG, "B is NULL");
+        }
+    }
+    return GEMM_OK;
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Can the direct global->LDS ring run this problem with this tile?
+bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
+    const int es = elem_size(q.in_type);
+    const int vec = 16 / es;
+    if (mfma) {
+        if (!(q.la == GEMM_ROW_MAJOR && q.lb == GEMM_COL_MAJOR)) { *why = "needs A row-major and B column-major (K-contiguous)"; return false; }
+    } else {
+        if (!(q.la == GEMM_ROW_MAJOR && q.lb == GEMM_ROW_MAJOR)) { *why = "needs A and B row-major"; return false; }
+    }
+    if (!aligned16(q.A) || !aligned16(q.B)) { *why = "A/B not 16-byte aligned"; return false; }
+    if (q.lda % vec || q.ldb % vec) { *why = "leading dimensions not a multiple of 16 bytes"; return false; }
+    if (q.K == 0 || q.K % t.bk) { *why = "K not a multiple of the slab depth"; return false; }
+    if (q.M < t.bm || q.N < t.bn) { *why = "problem smaller than the tile"; return false; }
+    // per-lane 32-bit offsets span up to one tile of rows (<= 256) of the operand
+    if ((q.lda * es) * 256 >= (int64_t(1) << 31) || (q.ldb * es) * 256 >= (int64_t(1) << 31)) {
+        *why = "leading dimension too large"; return false;
+    }
+    return true;
+}
+
+gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, GemmParams* gp) {
+    gemm_opts_t opts = {0, 0, 0, 0};
+    if (o) opts = *o;
+    if (opts.flags & ~GEMM_FLAG_NO_XCD_REMAP) return fail(GEMM_ERR_INVALID_ARG, "unknown flags 0x%x", opts.flags);
+    if (opts.nstage < 0 || opts.nstage > GEMM_MAX_NSTAGE) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d out of range", opts.nstage);
+    if (opts.kernel < 0 || opts.kernel > GEMM_KERNEL_SCALE) return fail(GEMM_ERR_INVALID_ARG, "kernel %d unknown", opts.kernel);
+    if (opts.tile < 0) return fail(GEMM_ERR_INVALID_ARG, "tile %d", opts.tile);
+    const bool mfma = q.in_type != gemm::DT_F32;
+    if (opts.kernel != 0) {
+        const bool k_mfma = opts.kernel == GEMM_KERNEL_MFMA_RING || opts.kernel == GEMM_KERNEL_MFMA_STAGED;
+        const bool k_valu = opts.kernel == GEMM_KERNEL_VALU_RING || opts.kernel == GEMM_KERNEL_VALU_STAGED;
+        if ((mfma && k_valu) || (!mfma && k_mfma))
+            return fail(GEMM_ERR_UNSUPPORTED, "kernel %d does not take this input type", opts.kernel);
+    }
+
+    memset(plan, 0, sizeof(*plan));
+    memset(gp, 0, sizeof(*gp));
+    gp->A = static_cast<const char*>(q.A);
+    gp->B = static_cast<const char*>(q.B);
+    gp->C = static_cast<char*>(const_cast<void*>(q.C));
+    gp->lda = q.lda; gp->ldb = q.ldb; gp->ldc = q.ldc;
+    gp->M = (int)q.M; gp->N = (int)q.N; gp->K = (int)q.K;
+    gp->alpha = q.alpha; gp->beta = q.beta;
+    gp->a_col = q.la == GEMM_COL_MAJOR;
+    gp->b_col = q.lb == GEMM_COL_MAJOR;
+    gp->out_type = q.c_type;
+    gp->xcd_remap = (opts.flags & GEMM_FLAG_NO_XCD_REMAP) ? 0 : 1;
+    gp->group_m = 8;
+    const int es = elem_size(q.in_type);
+    gp->a_vec = aligned16(q.A) && (q.lda * es) % 16 == 0;
+    gp->b_vec = aligned16(q.B) && (q.ldb * es) % 16 == 0;
+
+    if (q.M == 0 || q.N == 0) {
+        plan->kernel = GEMM_KERNEL_AUTO;
+        return GEMM_OK;  // nothing to do, nothing launched
+    }
+    if (q.K == 0 || q.alpha == 0.0f || opts.kernel == GEMM_KERNEL_SCALE) {
+        if (opts.kernel != 0 && opts.kernel != GEMM_KERNEL_SCALE)
+            return fail(GEMM_ERR_UNSUPPORTED, "K == 0 or alpha == 0 only scales C");
+        if (opts.kernel == GEMM_KERNEL_SCALE && !(q.K == 0 || q.alpha == 0.0f))
+            return fail(GEMM_ERR_UNSUPPORTED, "the scale kernel only runs when K == 0 or alpha == 0");
+        plan->kernel = GEMM_KERNEL_SCALE;
+        plan->threads = 256;
+        int64_t blocks = cdiv(q.M * q.N, 256);
+        plan->grid = blocks > 65536 ? 65536 : blocks;
+        return GEMM_OK;
+    }
+
+    int kernel = opts.kernel;
+    const Tile* t = nullptr;
+    const char* why = "";
+    if (kernel == 0) {
+        // Automatic: the direct ring when the operands allow it, else the staged loader.
+        if (!mfma) {
+            const Tile* big = find_tile(kValuRing, 1);
+            const Tile* small = find_tile(kValuRing, 3);
+            const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
+            const Tile* pick = (opts.tile ? find_tile(kValuRing, opts.tile) : (many ? big : small));
+            if (pick && ring_ok(q, *pick, false, &why)) { kernel = GEMM_KERNEL_VALU_RING; t = pick; }
+            else {
+                kernel = GEMM_KERNEL_VALU_STAGED;
+                t = find_tile(kValuStaged, many ? 1 : 3);
+            }
+        } else {
+            const Tile* big = find_tile(kMfmaRing, 1);
+            const Tile* mid = find_tile(kMfmaRing, 3);
+            const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
+            const Tile* pick = opts.tile ? find_tile(kMfmaRing, opts.tile) : (many ? big : mid);
+            if (pick && ring_ok(q, *pick, true, &why)) { kernel = GEMM_KERNEL_MFMA_RING; t = pick; }
+            else {
+                kernel = GEMM_KERNEL_MFMA_STAGED;
+                t = find_tile(kMfmaStaged, 1);
+            }
+        }
+    } else {
+        int id = opts.tile;
+        switch (kernel) {
+            case GEMM_KERNEL_VALU_RING: t = find_tile(kValuRing, id ? id : 1); break;
+            case GEMM_KERNEL_VALU_STAGED: t = find_tile(kValuStaged, id ? id : 1); break;
+            case GEMM_KERNEL_MFMA_RING: t = find_tile(kMfmaRing, id ? id : 1); break;
+            case GEMM_KERNEL_MFMA_STAGED: t = find_tile(kMfmaStaged, id ? id : 1); break;
+        }
+        if (!t) return fail(GEMM_ERR_UNSUPPORTED, "tile %d not available for kernel %d", opts.tile, kernel);
+        if ((kernel == GEMM_KERNEL_VALU_RING || kernel == GEMM_KERNEL_MFMA_RING) &&
+            !ring_ok(q, *t, kernel == GEMM_KERNEL_MFMA_RING, &why))
+            return fail(GEMM_ERR_UNSUPPORTED, "direct-to-LDS ring cannot run this problem: %s", why);
+    }
+    if (!t) return fail(GEMM_ERR_UNSUPPORTED, "no tile");
+
+    int S = opts.nstage ? opts.nstage : (t->max_stage >= 3 && kernel == GEMM_KERNEL_VALU_RING ? 3 : 2);
+    if (S > t->max_stage) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d not available for this tile (max %d)", S, t->max_stage);
+    if (S * t->stage_bytes > kLdsLimit)
+        return fail(GEMM_ERR_UNSUPPORTED, "ring of %d x %d bytes exceeds the %d bytes of LDS", S, t->stage_bytes, kLdsLimit);
+
+    plan->kernel = kernel;
+    plan->nstage = S;
+    plan->tile = t->id;
+    plan->bm = t->bm; plan->bn = t->bn; plan->bk = t->bk;
+    plan->threads = t->threads;
+    plan->lds_bytes = S * t->stage_bytes;
+    gp->tiles_m = (int)cdiv(q.M, t->bm);
+    gp->tiles_n = (int)cdiv(q.N, t->bn);
+    plan->grid = (int64_t)gp->tiles_m * gp->tiles_n;
+    if (plan->grid > INT32_MAX) return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
+    return GEMM_OK;
+}
+
+gemm_status_t run(const Problem& q, const gemm_opts_t* opts, hipStream_t stream) {
+    g_err[0] = 0;
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+    gemm_plan_t plan;
+    GemmParams gp;
+    s = choose(q, opts, &plan, &gp);
+    if (s != GEMM_OK) return s;
+    if (plan.grid == 0) return GEMM_OK;
+    hipError_t e = hipSuccess;
+    switch (plan.kernel) {
+        case GEMM_KERNEL_SCALE: e = gemm::launch_scale(gp, stream); break;
+        case GEMM_KERNEL_VALU_RING: e = gemm::launch_valu_ring(plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_VALU_STAGED: e = gemm::launch_valu_staged(plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_MFMA_RING: e = gemm::launch_mfma_ring(q.in_type, plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_MFMA_STAGED: e = gemm::launch_mfma_staged(q.in_type, plan.tile, plan.nstage, gp, stream); break;
+        default: return fail(GEMM_ERR_UNSUPPORTED, "internal: kernel %d", plan.kernel);
+    }
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GEMM_OK;
+}
+
+// ------------------------------------------------------------------ schedule recorder
+struct Recorder {
+    std::vector<int> ev;
+    void push(int t, int slab, int slot, int arg) { ev.insert(ev.end(), {t, slab, slot, arg}); }
+    void issue(int slab, int slot) { push(1, slab, slot, 0); }
+    template <int N> void wait_slabs() { push(2, -1, -1, N); }
+    void barrier() { push(3, -1, -1, 0); }
+    template <int BUF> void frag(int slab, int slot, int ks) { push(4, slab, slot, ks); }
+    template <int BUF> void math(int) {}
+    void wait_lds() { push(6, -1, -1, 0); }
+    void load(int slab) { push(1, slab, -1, 0); }
+    void write(int slab, int slot) { push(5, slab, slot, 0); }
+};
+
+template <int S, int KS>
+void rec_ring(Recorder& r, int numK) { gemm_sched::ring_mainloop<S, KS>(r, numK); }
+template <int S, int KS>
+void rec_staged(Recorder& r, int numK) { gemm_sched::staged_mainloop<S, KS>(r, numK); }
+
+template <int S>
+bool rec_ring_ks(Recorder& r, int ks, int numK) {
+    switch (ks) {
+        case 2: rec_ring<S, 2>(r, numK); return true;
+        case 4: rec_ring<S, 4>(r, numK); return true;
+        case 8: rec_ring<S, 8>(r, numK); return true;
+    }
+    return false;
+}
+template <int S>
+bool rec_staged_ks(Recorder& r, int ks, int numK) {
+    switch (ks) {
+        case 2: rec_staged<S, 2>(r, numK); return true;
+        case 4: rec_staged<S, 4>(r, numK); return true;
+        case 8: rec_staged<S, 8>(r, numK); return true;
+    }
+    return false;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_f32_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                          const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C,
+                          int64_t ldc, hipStream_t stream, const gemm_opts_t* opts) {
+    Problem q{gemm::DT_F32, gemm::DT_F32, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    return run(q, opts, stream);
+}
+
+static gemm_status_t half_entry(int in_type, gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                                float alpha, const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                                void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                                const gemm_opts_t* opts) {
+    g_err[0] = 0;
+    if (c_type != GEMM_F32 && (int)c_type != in_type)
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered by this entry point", (int)c_type);
+    Problem q{in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    return run(q, opts, stream);
+}
+
+gemm_status_t gemm_bf16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                           gemm_dtype_t c_type, int64_t ldc, hipStream_t stream, const gemm_opts_t* opts) {
+    return half_entry(gemm::DT_BF16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts);
+}
+
+gemm_status_t gemm_f16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                          gemm_dtype_t c_type, int64_t ldc, hipStream_t stream, const gemm_opts_t* opts) {
+    return half_entry(gemm::DT_F16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts);
+}
+
+gemm_status_t gemm_f32(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                       const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
+                       hipStream_t stream) {
+    return gemm_f32_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_bf16(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                        const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                        gemm_dtype_t c_type, int64_t ldc, hipStream_t stream) {
+    return gemm_bf16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_f16(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                       const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                       gemm_dtype_t c_type, int64_t ldc, hipStream_t stream) {
+    return gemm_f16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, nullptr);
+}
+
+gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
+                        int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float beta, const void* C, int64_t ldc, const gemm_opts_t* opts, gemm_plan_t* plan) {
+    g_err[0] = 0;
+    if (!plan) return fail(GEMM_ERR_INVALID_ARG, "plan is NULL");
+    if (in_type != GEMM_F32 && in_type != GEMM_BF16 && in_type != GEMM_F16)
+        return fail(GEMM_ERR_INVALID_ARG, "in_type %d", (int)in_type);
+    if (in_type == GEMM_F32 ? c_type != GEMM_F32 : (c_type != GEMM_F32 && c_type != in_type))
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered for in_type %d", (int)c_type, (int)in_type);
+    Problem q{(int)in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+    GemmParams gp;
+    return choose(q, opts, plan, &gp);
+}
+
+int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity) {
+    if (num_k < 0 || capacity < 0 || (capacity > 0 && !events)) return -1;
+    Recorder r;
+    bool ok = false;
+    if (kernel == GEMM_KERNEL_VALU_RING || kernel == GEMM_KERNEL_MFMA_RING) {
+        switch (nstage) {
+            case 1: ok = rec_ring_ks<1>(r, ksteps, num_k); break;
+            case 2: ok = rec_ring_ks<2>(r, ksteps, num_k); break;
+            case 3: ok = rec_ring_ks<3>(r, ksteps, num_k); break;
+            case 4: ok = rec_ring_ks<4>(r, ksteps, num_k); break;
+            case 5: ok = rec_ring_ks<5>(r, ksteps, num_k); break;
+        }
+    } else if (kernel == GEMM_KERNEL_VALU_STAGED || kernel == GEMM_KERNEL_MFMA_STAGED) {
+        switch (nstage) {
+            case 1: ok = rec_staged_ks<1>(r, ksteps, num_k); break;
+            case 2: ok = rec_staged_ks<2>(r, ksteps, num_k); break;
+        }
+    }
+    if (!ok) return -1;
+    const int n = (int)(r.ev.size() / 4);
+    const int w = n < capacity ? n : capacity;
+    if (w > 0) memcpy(events, r.ev.data(), sizeof(int) * 4 * (size_t)w);
+    return n;
+}
+
+const char* gemm_status_string(gemm_status_t s) {
+    switch (s) {
+        case GEMM_OK: return "GEMM_OK";
+        case GEMM_ERR_INVALID_ARG: return "GEMM_ERR_INVALID_ARG";
+        case GEMM_ERR_UNSUPPORTED: return "GEMM_ERR_UNSUPPORTED";
+        case GEMM_ERR_HIP: return "GEMM_ERR_HIP";
+    }
+    return "GEMM_ERR_UNKNOWN";
+}
+
+const char* gemm_last_error(void) { return g_err; }
+
+}  // extern "C"

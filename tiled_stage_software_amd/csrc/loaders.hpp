@@ -1,0 +1,220 @@
+// loaders.hpp -- global -> LDS slab loaders.
+//
+// Every kernel keeps, per ring slot, one LDS tile per operand made of LR "LDS rows" of
+// ROWB bytes.  A 16-byte chunk c of LDS row r sits at chunk position c ^ swz(r) when
+// the operand is swizzled (the swizzled shared-memory layout of section 5.2 of the
+// multi-stage page, here as an XOR on 16-byte chunks so that the MFMA / FMA fragment
+// reads of consecutive rows spread over all LDS banks).
+//
+//  * DirectLoader: global_load_lds_dwordx4 -- each lane's 16 bytes go from HBM straight
+//    into LDS without passing through registers (the role of the asynchronous copy of
+//    "Matrix multiplication" and of cp.async in the other pages).  The LDS destination
+//    of one wave instruction is 1 KiB contiguous, so the swizzle is produced by choosing
+//    which global chunk each lane fetches.  Requires the global operand to be
+//    contiguous along the LDS row, 16-byte aligned rows, and the whole tile in bounds.
+//  * StagedLoader: ordinary loads into registers, then ds_write.  Handles any layout
+//    (transposing when the global operand is contiguous across LDS rows), any
+//    alignment (element loads when 16-byte vectors are not legal) and ragged edges
+//    (out-of-range elements are written as zero, so they add +0 to every sum).
+#pragma once
+
+#include "common.hpp"
+
+namespace gemm {
+
+// Byte offset of element column `col` (in elements of size ES) of LDS row `r`.
+template <int ROWB, int ES, bool SWZ>
+__device__ __forceinline__ int lds_offset(int r, int col) {
+    constexpr int CPR = ROWB / 16;
+    const int byte = col * ES;
+    const int chunk = byte >> 4;
+    const int pc = SWZ ? (chunk ^ swz<CPR>(r)) : chunk;
+    return r * ROWB + (pc << 4) + (byte & 15);
+}
+
+// ------------------------------------------------------------------------------------
+// LR rows of ROWB bytes, loaded by NW waves, IPW copies of 1 KiB per wave per slab.
+template <int LR, int ROWB, int NW, bool SWZ>
+struct DirectLoader {
+    static constexpr int CPR = ROWB / 16;
+    static constexpr int RPI = 64 / CPR;            // LDS rows per copy instruction
+    static constexpr int IPW = LR / (RPI * NW);     // copies per wave per slab
+    static_assert(ROWB % 16 == 0 && CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row bytes");
+    static_assert(IPW >= 1 && IPW * RPI * NW == LR, "rows must split evenly over the waves");
+    static_assert(!SWZ || (RPI * NW) % 16 == 0, "swizzle must repeat between copies of a wave");
+
+    const char* base;      // uniform: address of LDS row 0, chunk 0 of slab 0
+    int64_t slab_step;     // uniform: bytes between consecutive slabs
+    uint32_t voff[IPW];    // per lane: global byte offset of this lane's chunk in copy i
+    int lds_wave;          // uniform: LDS byte offset of this wave's copy 0
+
+    // row_origin: global address of LDS row 0 / chunk 0 in slab 0; ld_bytes: bytes
+    // between consecutive LDS rows in global memory (the host keeps LR*ld_bytes < 2^31,
+    // so the per-lane offsets fit 32 bits and the copies use a scalar base + vector offset).
+    __device__ __forceinline__ void init(const char* row_origin, int64_t ld_bytes, int64_t slab_bytes) {
+        const int w = wave_id();
+        const int lane = lane_id();
+        const int lr = lane / CPR;
+        const int pc = lane % CPR;
+        const int r = w * RPI + lr;
+        const int c = SWZ ? (pc ^ swz<CPR>(r)) : pc;
+        base = row_origin;
+        slab_step = slab_bytes;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            voff[i] = (uint32_t)((int64_t)(r + i * RPI * NW) * ld_bytes + c * 16);
+        lds_wave = w * RPI * ROWB;
+    }
+    __device__ __forceinline__ void issue(int slab, LDS_AS char* lds_tile) const {
+        const char* g = base + (int64_t)slab * slab_step;
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            copy16_to_lds(g + voff[i], lds_tile + lds_wave + i * (RPI * NW * ROWB));
+    }
+};
+
+// ------------------------------------------------------------------------------------
+// Register-staged loader.  LDS tile: LR rows x LC elements (ES bytes each), row pitch
+// ROWB = LC*ES.  Global element (LDS row r, LDS col c) of slab s is at
+//   aligned    (TRANS = false, contiguous along LDS cols): X[(r0 + r)*ld + c0 + c]
+//   transposed (TRANS = true, contiguous along LDS rows):  X[(c0 + c)*ld + r0 + r]
+// where slab s advances c0 by LC, or -- for an operand whose slabs advance along the LDS
+// rows (`slab_rows`: the VALU B tile, LDS rows = k) -- r0 by LR.  Row indices are valid
+// below r_lim, column indices below c_lim.
+//
+// Per slab the loader takes one of two paths, chosen uniformly for the workgroup:
+// interior slabs with 16-byte-legal alignment use one vector load per 16 bytes; all
+// other slabs use element loads in which an out-of-range element reads element 0 of the
+// operand and is replaced by +0 (select, no lane-divergent branch), so ragged edges and
+// the K tail contribute exactly zero.
+template <int LR, int LC, int ES, int NT, bool SWZ, bool TRANS>
+struct StagedLoader {
+    static constexpr int VE = 16 / ES;               // elements per 16-byte vector
+    static constexpr int ROWB = LC * ES;
+    // aligned mode: chunks of VE along an LDS row
+    static constexpr int CH = LR * LC / VE / NT;     // vectors per thread per slab
+    static_assert(CH >= 1 && CH * VE * NT == LR * LC, "slab must split evenly over the threads");
+    // transposed mode: VE consecutive LDS rows x CHT consecutive LDS cols per thread
+    static constexpr int G = LR / VE;
+    static constexpr int CHT = LC * G / NT;
+    static_assert(!TRANS || CHT == CH, "both modes move the same number of vectors");
+    static_assert(!TRANS || (CHT * ES <= 16 && (16 % (CHT * ES)) == 0), "a transposed write must fit in one chunk");
+
+    u32x4 v[CH];
+    const char* X;
+    int64_t ld;          // elements
+    int r0, c0;          // tile origin (LDS row 0 / col 0 of slab 0), in the operand's index space
+    int r_lim, c_lim;    // valid extents
+    bool vec;            // 16-byte vector loads are legal (alignment)
+    bool slab_rows;      // slabs advance along LDS rows (else along LDS cols)
+
+    __device__ __forceinline__ void init(const char* X_, int64_t ld_, int r0_, int c0_, int r_lim_, int c_lim_,
+                                         bool vec_, bool slab_rows_) {
+        X = X_; ld = ld_; r0 = r0_; c0 = c0_; r_lim = r_lim_; c_lim = c_lim_;
+        vec = vec_; slab_rows = slab_rows_;
+    }
+
+    __device__ __forceinline__ uint32_t ld_elem(int64_t idx) const {
+        if constexpr (ES == 4) return reinterpret_cast<const uint32_t*>(X)[idx];
+        else return reinterpret_cast<const uint16_t*>(X)[idx];
+    }
+
+    // Thread's j-th vector: LDS row / col of its first element and the global index.
+    __device__ __forceinline__ void coords(int j, int rs, int cs, int& gr, int& gc, int64_t& idx) const {
+        const int tid = threadIdx.x;
+        if constexpr (!TRANS) {
+            const int q = tid + j * NT;
+            gr = rs + q / (LC / VE);
+            gc = cs + (q % (LC / VE)) * VE;
+            idx = (int64_t)gr * ld + gc;
+        } else {
+            gr = rs + (tid % G) * VE;
+            gc = cs + (tid / G) * CHT + j;
+            idx = (int64_t)gc * ld + gr;
+        }
+    }
+
+    __device__ __forceinline__ void load(int slab) {
+        const int rs = slab_rows ? r0 + slab * LR : r0;
+        const int cs = slab_rows ? c0 : c0 + slab * LC;
+        const bool interior = vec && rs + LR <= r_lim && cs + LC <= c_lim;
+        if (interior) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                int gr, gc;
+                int64_t idx;
+                coords(j, rs, cs, gr, gc, idx);
+                v[j] = *reinterpret_cast<const u32x4*>(X + idx * ES);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                int gr, gc;
+                int64_t idx;
+                coords(j, rs, cs, gr, gc, idx);
+                u32x4 t = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const bool ok = TRANS ? (gc < c_lim && gr + e < r_lim) : (gr < r_lim && gc + e < c_lim);
+                    uint32_t x = ld_elem(ok ? idx + e : 0);
+                    x = ok ? x : 0u;
+                    if constexpr (ES == 4) t[e] = x;
+                    else t[e >> 1] |= x << ((e & 1) * 16);
+                }
+                v[j] = t;
+            }
+        }
+    }
+
+    __device__ __forceinline__ uint32_t elem(int j, int e) const {
+        if constexpr (ES == 4) return v[j][e];
+        else return (v[j][e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+    }
+
+    __device__ __forceinline__ void write(LDS_AS char* lds_tile) const {
+        const int tid = threadIdx.x;
+        if constexpr (!TRANS) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                const int q = tid + j * NT;
+                const int r = q / (LC / VE);
+                const int c = (q % (LC / VE)) * VE;
+                *reinterpret_cast<LDS_AS u32x4*>(lds_tile + lds_offset<ROWB, ES, SWZ>(r, c)) = v[j];
+            }
+        } else {
+            const int grp = tid % G;
+            const int cb = (tid / G) * CHT;
+#pragma unroll
+            for (int e = 0; e < VE; ++e) {
+                const int r = grp * VE + e;
+                LDS_AS char* dst = lds_tile + lds_offset<ROWB, ES, SWZ>(r, cb);
+                if constexpr (CHT * ES == 16) {
+                    u32x4 w;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if constexpr (ES == 4) w[q] = elem(q, e);
+                        else w[q] = elem(2 * q, e) | (elem(2 * q + 1, e) << 16);
+                    }
+                    *reinterpret_cast<LDS_AS u32x4*>(dst) = w;
+                } else if constexpr (CHT * ES == 8) {
+                    u32x2 w;
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        if constexpr (ES == 4) w[q] = elem(q, e);
+                        else w[q] = elem(2 * q, e) | (elem(2 * q + 1, e) << 16);
+                    }
+                    *reinterpret_cast<LDS_AS u32x2*>(dst) = w;
+                } else if constexpr (CHT * ES == 4) {
+                    uint32_t w;
+                    if constexpr (ES == 4) w = elem(0, e);
+                    else w = elem(0, e) | (elem(1, e) << 16);
+                    *reinterpret_cast<LDS_AS uint32_t*>(dst) = w;
+                } else {
+                    *reinterpret_cast<LDS_AS uint16_t*>(dst) = (uint16_t)elem(0, e);
+                }
+            }
+        }
+    }
+};
+
+}  // namespace gemm

@@ -1,0 +1,234 @@
+"""ctypes binding of libgemm.so -- argument marshalling only.
+
+The functions named like the C ABI (``gemm_f32``, ``gemm_bf16``, ``gemm_f16``, their
+``_ex`` forms, ``gemm_plan``, ``gemm_schedule``, ``gemm_status_string``,
+``gemm_last_error``) take plain integers for device pointers and return the status
+code.  ``matmul`` is a convenience wrapper over torch tensors: it reads the layout and
+leading dimension of each operand from its strides and passes ``data_ptr()`` and the
+current HIP stream; every step of the computation runs in the library's kernels.
+
+There is no fallback: if libgemm.so cannot be loaded, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "lib", "libgemm.so")
+
+GEMM_OK, GEMM_ERR_INVALID_ARG, GEMM_ERR_UNSUPPORTED, GEMM_ERR_HIP = 0, 1, 2, 3
+GEMM_ROW_MAJOR, GEMM_COL_MAJOR = 0, 1
+GEMM_F32, GEMM_BF16, GEMM_F16 = 0, 1, 2
+(GEMM_KERNEL_AUTO, GEMM_KERNEL_VALU_RING, GEMM_KERNEL_VALU_STAGED, GEMM_KERNEL_MFMA_RING,
+ GEMM_KERNEL_MFMA_STAGED, GEMM_KERNEL_SCALE) = range(6)
+GEMM_FLAG_NO_XCD_REMAP = 1
+GEMM_MAX_NSTAGE = 5
+
+KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: "mfma_staged", 5: "scale"}
+
+# Symbols declared in include/libgemm.h.
+EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
+           "gemm_plan", "gemm_schedule", "gemm_status_string", "gemm_last_error")
+
+
+class GemmOpts(ctypes.Structure):
+    _fields_ = [("nstage", ctypes.c_int), ("kernel", ctypes.c_int), ("tile", ctypes.c_int),
+                ("flags", ctypes.c_int)]
+
+
+class GemmPlan(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("nstage", ctypes.c_int), ("tile", ctypes.c_int),
+                ("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
+                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("grid", ctypes.c_int64)]
+
+    def as_dict(self):
+        d = {f: getattr(self, f) for f, _ in self._fields_}
+        d["kernel_name"] = KERNEL_NAMES.get(self.kernel, str(self.kernel))
+        return d
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{status_name(status)}: {msg}")
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load():
+    """Load libgemm.so (built in-tree by ``tiled_stage_software_amd.build``)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it first "
+                               "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(LIB_PATH)
+        i64, vp, i32, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+        base = [i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp]
+        lib.gemm_f32.argtypes = base + [i64, vp]
+        lib.gemm_f32_ex.argtypes = base + [i64, vp, ctypes.POINTER(GemmOpts)]
+        for name in ("gemm_bf16", "gemm_f16"):
+            getattr(lib, name).argtypes = base + [i32, i64, vp]
+            getattr(lib, name + "_ex").argtypes = base + [i32, i64, vp, ctypes.POINTER(GemmOpts)]
+        for name in ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex"):
+            getattr(lib, name).restype = i32
+        lib.gemm_plan.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                                  ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlan)]
+        lib.gemm_plan.restype = i32
+        lib.gemm_schedule.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int), i32]
+        lib.gemm_schedule.restype = i32
+        lib.gemm_status_string.argtypes = [i32]
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_last_error.argtypes = []
+        lib.gemm_last_error.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def _opts(nstage=0, kernel=0, tile=0, flags=0) -> Optional[GemmOpts]:
+    if not (nstage or kernel or tile or flags):
+        return None
+    return GemmOpts(int(nstage), int(kernel), int(tile), int(flags))
+
+
+def _ref(o):
+    return ctypes.byref(o) if o is not None else None
+
+
+# ------------------------------------------------------------------ C ABI names
+
+def gemm_f32(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return load().gemm_f32(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_bf16(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0) -> int:
+    return load().gemm_bf16(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream)
+
+
+def gemm_f16(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0) -> int:
+    return load().gemm_f16(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream)
+
+
+def gemm_f32_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, opts=None) -> int:
+    return load().gemm_f32_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, _ref(opts))
+
+
+def gemm_bf16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None) -> int:
+    return load().gemm_bf16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts))
+
+
+def gemm_f16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None) -> int:
+    return load().gemm_f16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts))
+
+
+def gemm_plan(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, opts=None):
+    """Returns (status, GemmPlan)."""
+    plan = GemmPlan()
+    s = load().gemm_plan(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                         _ref(opts), ctypes.byref(plan))
+    return s, plan
+
+
+def gemm_schedule(kernel, nstage, num_k, ksteps):
+    """Event list [(type, slab, slot, arg), ...] of the kernel family's K loop, or None."""
+    lib = load()
+    n = lib.gemm_schedule(kernel, nstage, num_k, ksteps, None, 0)
+    if n < 0:
+        return None
+    buf = (ctypes.c_int * (4 * max(n, 1)))()
+    lib.gemm_schedule(kernel, nstage, num_k, ksteps, buf, n)
+    return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def gemm_status_string(s: int) -> str:
+    return load().gemm_status_string(int(s)).decode()
+
+
+def gemm_last_error() -> str:
+    return load().gemm_last_error().decode()
+
+
+def status_name(s: int) -> str:
+    try:
+        return gemm_status_string(s)
+    except Exception:  # library not loadable: still give the number
+        return f"status {s}"
+
+
+def check(status: int):
+    if status != GEMM_OK:
+        raise GemmError(status, gemm_last_error())
+
+
+# ------------------------------------------------------------------ torch convenience
+
+def _layout_of(t, rows, cols):
+    """(layout, ld) of a 2-D tensor view, or None if it is neither row- nor column-major."""
+    s0, s1 = t.stride()
+    if cols == 1 and rows == 1:
+        return GEMM_ROW_MAJOR, 1
+    if s1 == 1 and (rows == 1 or s0 >= cols):
+        return GEMM_ROW_MAJOR, max(s0, cols) if rows > 1 else cols
+    if s0 == 1 and (cols == 1 or s1 >= rows):
+        return GEMM_COL_MAJOR, max(s1, rows) if cols > 1 else rows
+    return None
+
+
+def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, stream=None,
+           nstage: int = 0, kernel: int = 0, tile: int = 0, flags: int = 0):
+    """C = alpha*A@B + beta*C on device tensors (A: M x K, B: K x N, any of the two
+    layouts per operand, C row-major).  Returns C."""
+    import torch
+    if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
+        raise ValueError(f"shapes {tuple(A.shape)} @ {tuple(B.shape)}")
+    if A.dtype != B.dtype:
+        raise ValueError("A and B must have the same dtype")
+    M, K = A.shape
+    N = B.shape[1]
+    la = _layout_of(A, M, K)
+    lb = _layout_of(B, K, N)
+    if la is None or lb is None:
+        raise ValueError("operands must be row- or column-major views")
+    if C is None:
+        if beta != 0.0:
+            raise ValueError("beta != 0 needs C")
+        if out_dtype is None:
+            out_dtype = A.dtype
+        C = torch.empty((M, N), dtype=out_dtype, device=A.device)
+    if C.dim() != 2 or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
+        raise ValueError("C must be an M x N row-major view")
+    ldc = max(C.stride(0), N) if M > 1 else max(N, 1)
+    st = stream if stream is not None else torch.cuda.current_stream(A.device).cuda_stream
+    o = _opts(nstage, kernel, tile, flags)
+    if A.dtype == torch.float32:
+        if C.dtype != torch.float32:
+            raise ValueError("fp32 inputs give fp32 C")
+        s = gemm_f32_ex(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
+                        beta, C.data_ptr(), ldc, st, o)
+    elif A.dtype in (torch.bfloat16, torch.float16):
+        ct = {torch.float32: GEMM_F32, torch.bfloat16: GEMM_BF16, torch.float16: GEMM_F16}[C.dtype]
+        fn = gemm_bf16_ex if A.dtype == torch.bfloat16 else gemm_f16_ex
+        s = fn(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
+               beta, C.data_ptr(), ct, ldc, st, o)
+    else:
+        raise ValueError(f"unsupported dtype {A.dtype}")
+    check(s)
+    return C
+
+
+def gemm_operands(in_dtype: str, out_dtype: str, la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb,
+                  beta, C_ptr, ldc, stream=0, nstage=0, kernel=0, tile=0, flags=0) -> int:
+    """Dispatch on dtype names ('f32' / 'bf16' / 'f16') with raw pointers."""
+    o = _opts(nstage, kernel, tile, flags)
+    if in_dtype == "f32":
+        return gemm_f32_ex(la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream, o)
+    ct = {"f32": GEMM_F32, "bf16": GEMM_BF16, "f16": GEMM_F16}[out_dtype]
+    fn = gemm_bf16_ex if in_dtype == "bf16" else gemm_f16_ex
+    return fn(la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ct, ldc, stream, o)
