@@ -109,16 +109,15 @@ def cpu_baseline(w: Workload, target_s: float, nthreads: int):
     from oracle import oracle
     p = w.p
     la, lb = p.A.layout == inputs.COL, p.B.layout == inputs.COL
-    # probe with a few rows, then size the sample to ~target_s seconds
-    probe_rows = [0, p.M - 1]
+    # probe with one row per thread, then size the sample to ~target_s seconds
+    threads = oracle.max_threads(nthreads)
+    probe_rows = np.linspace(0, p.M - 1, min(p.M, threads)).astype(np.int64).tolist()
     t0 = time.perf_counter()
     oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
                     None if p.C0 is None else p.C0.storage, p.N, rows=probe_rows, nthreads=nthreads)
     dt = max(time.perf_counter() - t0, 1e-4)
-    per_row = dt / len(probe_rows)
-    threads = oracle.max_threads(nthreads)
-    n = int(target_s / per_row * min(threads, 8) / 2)
-    n = max(threads, min(p.M, n))
+    n = int(target_s / dt * len(probe_rows))
+    n = max(min(p.M, threads), min(p.M, n))
     rows = sorted(set(np.linspace(0, p.M - 1, n).astype(np.int64).tolist()))
     t0 = time.perf_counter()
     ref = oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
@@ -162,6 +161,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--only", action="store_true", help="time only the headline launches (for profiling)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="instead of the GEMM, run a plain device copy kernel of this many MiB "
+                         "(read + write) a few times: the reference for scaling HBM counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -173,6 +175,16 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.rand(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration": {"read_bytes": n * 4, "write_bytes": n * 4, "launches": 5,
+                                               "kernel": "torch.mul(src, 1.0, out=dst), fp32"}}), flush=True)
+        return
     lg.load()
     src_hash = kernel_source_hash()
 

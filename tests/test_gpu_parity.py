@@ -61,6 +61,9 @@ FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= 
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, 2, 512, 512, 256),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 3, 2, 256, 384, 128),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, 4, 256, 512, 256),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 7, 2, 512, 256, 256),
+    ("f16", "f32", ROW, COL, K_MFMA_RING, 8, 2, 256, 512, 256),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, 4, 256, 256, 256),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, 2, 200, 136, 77),
     ("f16", "f16", COL, ROW, K_MFMA_STAGED, 1, 1, 129, 257, 40),
 ]
@@ -196,6 +199,7 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, [1, 2, 3, 4], 512, 768, 640),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 3, [1, 2, 3, 4], 384, 256, 704),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, [3, 4], 512, 768, 640),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
 ]
@@ -344,3 +348,32 @@ def test_matmul_wrapper_on_strided_views():
     ref = oracle.gemm_f64(False, True, 300, 150, 200, 1.0, A.cpu(), 200, Bt.cpu(), 200)
     err = oracle.normalized_error(C.cpu().double().numpy(), ref, 200, A.abs().max().item(), Bt.abs().max().item())
     assert err <= 1e-5
+
+
+# --------------------------------------------------------------- every built variant
+
+def _planned_variants():
+    """Every (kernel family, tile, nstage) the planner accepts for a problem that fits
+    all tiles; each must launch and agree with the oracle."""
+    out = []
+    for kern, dt, la, lb in ((K_MFMA_RING, "bf16", ROW, COL), (K_MFMA_STAGED, "f16", ROW, ROW),
+                             (K_VALU_RING, "f32", ROW, ROW), (K_VALU_STAGED, "f32", COL, ROW)):
+        for tile in range(1, 13):
+            for S in range(1, 6):
+                code = {"f32": 0, "bf16": 1, "f16": 2}[dt]
+                M, N, K = 512, 512, 384
+                s, plan = lg.gemm_plan(code, code, la, lb, M, N, K, 1.0, 16, K if la == ROW else M, 16,
+                                       N if lb == ROW else K, 0.0, 16, N,
+                                       lg.GemmOpts(S, kern, tile, 0))
+                if s == lg.GEMM_OK:
+                    out.append((kern, dt, la, lb, tile, S))
+    return out
+
+
+@pytest.mark.parametrize("v", _planned_variants(), ids=lambda v: f"k{v[0]}-{v[1]}-t{v[4]}-s{v[5]}")
+def test_every_planned_variant_launches_and_matches(v):
+    kern, dt, la, lb, tile, S = v
+    say(f"[variant] kernel={kern} {dt} tile={tile} nstage={S}")
+    p = problem(dt, dt if dt != "f32" else "f32", 512, 512, 384, la, lb, dist="int2", seed=61)
+    got = run(p, kernel=kern, tile=tile, nstage=S)
+    assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))

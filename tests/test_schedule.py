@@ -28,6 +28,7 @@ def simulate(events, S, numK, ksteps, staged):
     computed = []
     barriers = 0
     waits = []
+    parts_seen = {}         # slab -> [parts issued, parts]
     for (t, slab, slot, arg) in events:
         if t == ISSUE:
             if staged:
@@ -36,8 +37,15 @@ def simulate(events, S, numK, ksteps, staged):
                 continue
             assert 0 <= slot < S
             assert slot_reads.get(slot) is None, f"WAR: copy of slab {slab} into slot {slot} while it may be read"
-            slot_slab[slot] = slab
-            in_flight.append(slab)
+            part, parts = arg & 0xff, max(1, arg >> 8)
+            if part == 0:
+                assert slab not in parts_seen, f"slab {slab} issued twice"
+                parts_seen[slab] = [0, parts]
+                slot_slab[slot] = slab
+                in_flight.append(slab)
+            else:
+                assert slot_slab.get(slot) == slab and parts_seen[slab][0] == part, "parts in order, same slot"
+            parts_seen[slab][0] += 1
         elif t == WRITE:
             assert staged and slab in reg_loaded, "write before the global load"
             assert slot_reads.get(slot) is None, f"WAR: write of slab {slab} into slot {slot} while it may be read"
@@ -45,6 +53,8 @@ def simulate(events, S, numK, ksteps, staged):
             written_pending.add(slab)
         elif t == WAIT:
             assert arg >= 0
+            # the count is in whole slabs: every slab in flight must be fully issued
+            assert all(parts_seen[x][0] == parts_seen[x][1] for x in in_flight), "wait with a half-issued slab"
             waits.append((len(in_flight), arg))
             while len(in_flight) > arg:
                 complete.add(in_flight.pop(0))
@@ -74,16 +84,16 @@ def simulate(events, S, numK, ksteps, staged):
 
 @pytest.mark.parametrize("kernel", [lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("ksteps", [2, 4, 8])
-def test_ring_protocol(kernel, S, ksteps):
+@pytest.mark.parametrize("ksteps,cs", [(2, 1), (4, 1), (8, 1), (4, 2), (4, 3), (8, 3)])
+def test_ring_protocol(kernel, S, ksteps, cs):
     for numK in list(range(0, 12)) + [33, 40]:
-        ev = lg.gemm_schedule(kernel, S, numK, ksteps)
+        ev = lg.gemm_schedule(kernel, S, numK, ksteps + 16 * (cs - 1))
         assert ev is not None
         barriers, waits = simulate(ev, S, numK, ksteps, staged=False)
         if numK == 0:
             assert ev == []
             continue
-        issues = [e for e in ev if e[0] == ISSUE]
+        issues = [e for e in ev if e[0] == ISSUE and (e[3] & 0xff) == 0]
         assert [e[1] for e in issues] == list(range(numK))
         assert all(e[2] == e[1] % S for e in issues), "ring slot = slab mod nStage"
         if S == 1:
@@ -92,7 +102,7 @@ def test_ring_protocol(kernel, S, ksteps):
             assert barriers == numK, "ring: one barrier per slab"
             # prologue: min(S-1, numK) copies before the first wait
             first_wait = next(i for i, e in enumerate(ev) if e[0] == WAIT)
-            assert sum(1 for e in ev[:first_wait] if e[0] == ISSUE) == min(S - 1, numK)
+            assert sum(1 for e in ev[:first_wait] if e[0] == ISSUE and (e[3] & 0xff) == 0) == min(S - 1, numK)
             # wait for the oldest: in steady state S-2 slabs stay in flight
             if numK >= S + 1:
                 assert max(a for _, a in waits) == S - 2
@@ -133,6 +143,8 @@ def test_bad_arguments():
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 6, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 3, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 3) is None
+    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 2 + 16) is None      # 2 copy steps, 2 k-steps
+    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 2, 4, 4 + 16) is None
     assert lg.gemm_schedule(99, 2, 4, 4) is None
 
 
@@ -151,12 +163,18 @@ def _planted(events, kind):
                 break
     elif kind == "no_wait_lds":
         ev = [e for e in ev if e[0] != WAIT_LDS]
+    elif kind == "late_part":
+        # move the second part of slab 3's copy behind the next wait
+        j = next(j for j, e in enumerate(ev) if e[0] == ISSUE and e[1] == 3 and (e[3] & 0xff) == 1)
+        part = ev.pop(j)
+        w = next(k for k in range(j, len(ev)) if ev[k][0] == WAIT)
+        ev.insert(w + 1, part)
     return ev
 
 
-@pytest.mark.parametrize("kind", ["no_barrier", "wait_too_little", "wrong_slot", "no_wait_lds"])
+@pytest.mark.parametrize("kind", ["no_barrier", "wait_too_little", "wrong_slot", "no_wait_lds", "late_part"])
 def test_simulator_catches_planted_bugs(kind):
-    ev = lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 3, 8, 4)
+    ev = lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 3, 8, 4 + 16)
     simulate(ev, 3, 8, 4, staged=False)
     with pytest.raises(AssertionError):
         simulate(_planted(ev, kind), 3, 8, 4, staged=False)

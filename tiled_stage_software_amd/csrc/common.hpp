@@ -60,8 +60,10 @@ __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory
 // budgets registers for the occupancy the ring actually permits.
 constexpr int occupancy_waves(int threads, int lds_bytes, int cap) {
     const int wg = lds_bytes > 0 ? 163840 / lds_bytes : 32;
+    const int need = (threads + 255) / 256;  // one workgroup alone puts this many waves on a SIMD
     int w = wg * (threads / 64) / 4;
     if (w > cap) w = cap;
+    if (w < need) w = need;
     if (w < 1) w = 1;
     return w;
 }

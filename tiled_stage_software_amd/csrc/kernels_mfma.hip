@@ -90,14 +90,29 @@ struct MfmaCompute {
             fb[BUF][j] = *reinterpret_cast<LDS_AS const frag_t*>(st + b_off[ks] + j * 32 * ROWB);
     }
 
-    template <int BUF>
+    // The MFMAs of one k-step.  COPIES global->LDS copies and the next k-step's TM+TN
+    // fragment reads were issued in program order just before; the scheduling groups
+    // interleave them with the first MFMAs (one fragment read and COPIES/(TM+TN) copies
+    // after each MFMA) so that their latency runs under the remaining MFMAs instead of
+    // stalling the next k-step.
+    template <int BUF, int COPIES>
     __device__ __forceinline__ void math() {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
             for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(fb[BUF][j], fa[BUF][i], acc[i][j]);
-        // keep the k-step structure: the fragment loads issued before this math stay
-        // ahead of it and the next k-step's loads are not hoisted above it
+        constexpr int NF = TM + TN;
+        constexpr int NM = TM * TN;
+        constexpr int CPM = (COPIES + NF - 1) / NF;
+        static_assert(NM >= NF, "at least one MFMA per fragment read");
+#pragma unroll
+        for (int i = 0; i < NF; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            if constexpr (CPM > 0) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);  // VMEM read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, NM - NF, 0);
+        // keep the k-step structure: nothing of the next k-step is hoisted above here
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -141,10 +156,14 @@ struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     DirectLoader<BN, C::ROWB, NW, true> lb;
     static constexpr int L = DirectLoader<BM, C::ROWB, NW, true>::IPW + DirectLoader<BN, C::ROWB, NW, true>::IPW;
 
-    __device__ __forceinline__ void issue(int slab, int slot) {
+    // Part `part` of `parts` of the copy of slab `slab` into ring slot `slot`: the L
+    // copies of this wave (A's first, then B's) are split into equal consecutive runs.
+    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
         LDS_AS char* st = this->smem + slot * C::STAGE;
-        la.issue(slab, st);
-        lb.issue(slab, st + C::A_BYTES);
+        const int c0 = part * L / parts, c1 = (part + 1) * L / parts;
+        constexpr int LA_N = decltype(la)::IPW;
+        la.issue(slab, st, c0, c1 < LA_N ? c1 : LA_N);
+        lb.issue(slab, st + C::A_BYTES, c0 > LA_N ? c0 - LA_N : 0, c1 - LA_N);
     }
     template <int N>
     __device__ __forceinline__ void wait_slabs() { wait_vm<N * L>(); }
@@ -152,11 +171,11 @@ struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF>
-    __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
+    template <int BUF, int CS>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, CS ? (L + CS - 1) / CS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int CS>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
     occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, (BM / WM) * (BN / WN) > 64 * 64 ? 1 : 2))))
 void mfma_ring_kernel(const GemmParams p) {
@@ -173,7 +192,7 @@ void mfma_ring_kernel(const GemmParams p) {
     ops.init((LDS_AS char*)(smem_raw));
     ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
     ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-    gemm_sched::ring_mainloop<S, Ops::KS>(ops, p.K / BK);
+    gemm_sched::ring_mainloop<S, Ops::KS, CS>(ops, p.K / BK);
     ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
 }
 
@@ -200,8 +219,8 @@ struct MfmaStagedOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF>
-    __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
+    template <int BUF, int COPIES>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, 0>(); }
 };
 
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool AT, bool BT>
@@ -223,10 +242,10 @@ void mfma_staged_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------- launch tables
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int CS = 1>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, CS>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
@@ -262,6 +281,26 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2>(p, st);
             if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3>(p, st);
             if (S == 4) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 4>(p, st);
+            break;
+        case 4:  // 256x256x64, copies of a slab spread over 2 k-steps
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, 2>(p, st);
+            break;
+        case 5:  // 256x256x64, copies spread over 3 k-steps
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, 3>(p, st);
+            break;
+        case 6:  // 128x128x64, copies spread over 2 k-steps
+            if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2, 2>(p, st);
+            if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, 2>(p, st);
+            break;
+        case 7:  // 256x256x64, 2x4 waves of 128x64 (two waves per SIMD)
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 4, 2>(p, st);
+            break;
+        case 8:  // 256x256x64, 4x2 waves of 64x128 (two waves per SIMD)
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 4, 2, 2>(p, st);
+            break;
+        case 9:  // 256x256x32, 2x4 waves of 128x64, deeper ring
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4>(p, st);
             break;
     }
     return hipErrorInvalidValue;

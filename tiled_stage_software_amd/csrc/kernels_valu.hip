@@ -135,10 +135,14 @@ struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN> {
     LA la;
     LB lb;
 
-    __device__ __forceinline__ void issue(int slab, int slot) {
+    // Part `part` of `parts` of the copy of slab `slab` into ring slot `slot`: the L
+    // copies of this wave (A's first, then B's) are split into equal consecutive runs.
+    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
         LDS_AS char* st = this->smem + slot * C::STAGE;
-        la.issue(slab, st);
-        lb.issue(slab, st + C::A_BYTES);
+        const int c0 = part * L / parts, c1 = (part + 1) * L / parts;
+        constexpr int LA_N = decltype(la)::IPW;
+        la.issue(slab, st, c0, c1 < LA_N ? c1 : LA_N);
+        lb.issue(slab, st + C::A_BYTES, c0 > LA_N ? c0 - LA_N : 0, c1 - LA_N);
     }
     template <int N>
     __device__ __forceinline__ void wait_slabs() { wait_vm<N * L>(); }
@@ -146,7 +150,7 @@ struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF>
+    template <int BUF, int COPIES>
     __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
 };
 
@@ -166,7 +170,7 @@ void valu_ring_kernel(const GemmParams p) {
     // A row-major: LDS row m <- A[m][k0 .. k0+BK); B row-major: LDS row k <- B[k][n0 .. n0+BN).
     ops.la.init(p.A + (int64_t)m0 * p.lda * 4, p.lda * 4, BK * 4);
     ops.lb.init(p.B + (int64_t)n0 * 4, p.ldb * 4, (int64_t)BK * p.ldb * 4);
-    gemm_sched::ring_mainloop<S, Ops::KS>(ops, p.K / BK);
+    gemm_sched::ring_mainloop<S, Ops::KS, 1>(ops, p.K / BK);
     ops.epilogue(p, m0, n0, m_keep, n_keep);
 }
 
@@ -192,7 +196,7 @@ struct ValuStagedOps : ValuCompute<BM, BN, BK, TM, TN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF>
+    template <int BUF, int COPIES>
     __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
 };
 

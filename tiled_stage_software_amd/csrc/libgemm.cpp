@@ -29,27 +29,37 @@ gemm_status_t fail(gemm_status_t s, const char* fmt, ...) {
 }
 
 struct Tile {
-    int id, bm, bn, bk, threads, max_stage;
+    int id, bm, bn, bk, threads;
+    int stages;       // bit s set: nstage = s is instantiated
+    int def_stage;    // default nstage
     int stage_bytes;  // LDS per ring slot
 };
 
+constexpr int S1 = 1 << 1, S2 = 1 << 2, S3 = 1 << 3, S4 = 1 << 4;
+
 // Instantiated tiles of each family (must match the launch tables of the kernels).
 const Tile kValuRing[] = {
-    {1, 128, 64, 16, 128, 4, (128 * 16 + 16 * 64) * 4},
-    {2, 64, 64, 16, 256, 4, (64 * 16 + 16 * 64) * 4},
-    {3, 32, 32, 16, 64, 4, (32 * 16 + 16 * 32) * 4},
+    {1, 128, 64, 16, 128, S1 | S2 | S3 | S4, 3, (128 * 16 + 16 * 64) * 4},
+    {2, 64, 64, 16, 256, S1 | S2 | S3 | S4, 2, (64 * 16 + 16 * 64) * 4},
+    {3, 32, 32, 16, 64, S1 | S2 | S3 | S4, 2, (32 * 16 + 16 * 32) * 4},
 };
 const Tile kValuStaged[] = {
-    {1, 128, 64, 16, 128, 2, (128 * 16 + 16 * 64) * 4},
-    {3, 32, 32, 16, 64, 2, (32 * 16 + 16 * 32) * 4},
+    {1, 128, 64, 16, 128, S1 | S2, 2, (128 * 16 + 16 * 64) * 4},
+    {3, 32, 32, 16, 64, S1 | S2, 2, (32 * 16 + 16 * 32) * 4},
 };
 const Tile kMfmaRing[] = {
-    {1, 256, 256, 64, 256, 2, (256 + 256) * 64 * 2},
-    {2, 256, 256, 32, 256, 4, (256 + 256) * 32 * 2},
-    {3, 128, 128, 64, 256, 4, (128 + 128) * 64 * 2},
+    {1, 256, 256, 64, 256, S1 | S2, 2, (256 + 256) * 64 * 2},
+    {2, 256, 256, 32, 256, S1 | S2 | S3 | S4, 3, (256 + 256) * 32 * 2},
+    {3, 128, 128, 64, 256, S1 | S2 | S3 | S4, 2, (128 + 128) * 64 * 2},
+    {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies over 2 k-steps
+    {5, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies over 3 k-steps
+    {6, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},     // copies over 2 k-steps
+    {7, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves, 128x64 each
+    {8, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves, 64x128 each
+    {9, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},     // 8 waves, BK 32
 };
 const Tile kMfmaStaged[] = {
-    {1, 128, 128, 32, 256, 2, (128 + 128) * 32 * 2},
+    {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
 };
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
@@ -210,8 +220,9 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     }
     if (!t) return fail(GEMM_ERR_UNSUPPORTED, "no tile");
 
-    int S = opts.nstage ? opts.nstage : (t->max_stage >= 3 && kernel == GEMM_KERNEL_VALU_RING ? 3 : 2);
-    if (S > t->max_stage) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d not available for this tile (max %d)", S, t->max_stage);
+    int S = opts.nstage ? opts.nstage : t->def_stage;
+    if (!(t->stages & (1 << S)))
+        return fail(GEMM_ERR_UNSUPPORTED, "nstage %d not built for tile %d of kernel %d", S, t->id, kernel);
     if (S * t->stage_bytes > kLdsLimit)
         return fail(GEMM_ERR_UNSUPPORTED, "ring of %d x %d bytes exceeds the %d bytes of LDS", S, t->stage_bytes, kLdsLimit);
 
@@ -254,27 +265,34 @@ gemm_status_t run(const Problem& q, const gemm_opts_t* opts, hipStream_t stream)
 struct Recorder {
     std::vector<int> ev;
     void push(int t, int slab, int slot, int arg) { ev.insert(ev.end(), {t, slab, slot, arg}); }
-    void issue(int slab, int slot) { push(1, slab, slot, 0); }
     template <int N> void wait_slabs() { push(2, -1, -1, N); }
     void barrier() { push(3, -1, -1, 0); }
     template <int BUF> void frag(int slab, int slot, int ks) { push(4, slab, slot, ks); }
-    template <int BUF> void math(int) {}
+    template <int BUF, int COPIES> void math(int) {}
     void wait_lds() { push(6, -1, -1, 0); }
+    void issue(int slab, int slot, int part, int parts) { push(1, slab, slot, part | (parts << 8)); }
     void load(int slab) { push(1, slab, -1, 0); }
     void write(int slab, int slot) { push(5, slab, slot, 0); }
 };
 
 template <int S, int KS>
-void rec_ring(Recorder& r, int numK) { gemm_sched::ring_mainloop<S, KS>(r, numK); }
+void rec_ring(Recorder& r, int numK, int cs) {
+    if (cs == 1) gemm_sched::ring_mainloop<S, KS, 1>(r, numK);
+    else if constexpr (KS > 2) {
+        if (cs == 2) gemm_sched::ring_mainloop<S, KS, 2>(r, numK);
+        else if (cs == 3) gemm_sched::ring_mainloop<S, KS, 3>(r, numK);
+    }
+}
 template <int S, int KS>
 void rec_staged(Recorder& r, int numK) { gemm_sched::staged_mainloop<S, KS>(r, numK); }
 
 template <int S>
-bool rec_ring_ks(Recorder& r, int ks, int numK) {
+bool rec_ring_ks(Recorder& r, int ks, int numK, int cs) {
+    if (cs < 1 || cs >= ks || cs > 3) return false;
     switch (ks) {
-        case 2: rec_ring<S, 2>(r, numK); return true;
-        case 4: rec_ring<S, 4>(r, numK); return true;
-        case 8: rec_ring<S, 8>(r, numK); return true;
+        case 2: rec_ring<S, 2>(r, numK, cs); return true;
+        case 4: rec_ring<S, 4>(r, numK, cs); return true;
+        case 8: rec_ring<S, 8>(r, numK, cs); return true;
     }
     return false;
 }
@@ -360,15 +378,19 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
     if (num_k < 0 || capacity < 0 || (capacity > 0 && !events)) return -1;
     Recorder r;
     bool ok = false;
+    // ksteps = k-steps per slab + 16 * (copy steps - 1) for ring kernels
+    const int cs = 1 + (ksteps >> 4);
+    ksteps &= 15;
     if (kernel == GEMM_KERNEL_VALU_RING || kernel == GEMM_KERNEL_MFMA_RING) {
         switch (nstage) {
-            case 1: ok = rec_ring_ks<1>(r, ksteps, num_k); break;
-            case 2: ok = rec_ring_ks<2>(r, ksteps, num_k); break;
-            case 3: ok = rec_ring_ks<3>(r, ksteps, num_k); break;
-            case 4: ok = rec_ring_ks<4>(r, ksteps, num_k); break;
-            case 5: ok = rec_ring_ks<5>(r, ksteps, num_k); break;
+            case 1: ok = rec_ring_ks<1>(r, ksteps, num_k, cs); break;
+            case 2: ok = rec_ring_ks<2>(r, ksteps, num_k, cs); break;
+            case 3: ok = rec_ring_ks<3>(r, ksteps, num_k, cs); break;
+            case 4: ok = rec_ring_ks<4>(r, ksteps, num_k, cs); break;
+            case 5: ok = rec_ring_ks<5>(r, ksteps, num_k, cs); break;
         }
     } else if (kernel == GEMM_KERNEL_VALU_STAGED || kernel == GEMM_KERNEL_MFMA_STAGED) {
+        if (cs != 1) return -1;
         switch (nstage) {
             case 1: ok = rec_staged_ks<1>(r, ksteps, num_k); break;
             case 2: ok = rec_staged_ks<2>(r, ksteps, num_k); break;

@@ -65,11 +65,13 @@ struct DirectLoader {
             voff[i] = (uint32_t)((int64_t)(r + i * RPI * NW) * ld_bytes + c * 16);
         lds_wave = w * RPI * ROWB;
     }
-    __device__ __forceinline__ void issue(int slab, LDS_AS char* lds_tile) const {
+    // Copies [i0, i1) of this wave's IPW copies of slab `slab` (compile-time range
+    // after unrolling).
+    __device__ __forceinline__ void issue(int slab, LDS_AS char* lds_tile, int i0, int i1) const {
         const char* g = base + (int64_t)slab * slab_step;
 #pragma unroll
         for (int i = 0; i < IPW; ++i)
-            copy16_to_lds(g + voff[i], lds_tile + lds_wave + i * (RPI * NW * ROWB));
+            if (i >= i0 && i < i1) copy16_to_lds(g + voff[i], lds_tile + lds_wave + i * (RPI * NW * ROWB));
     }
 };
 

@@ -51,16 +51,19 @@ enum { BODY_MAIN = 0, BODY_TAIL = 1, BODY_LAST = 2 };
 // One slab of KS k-steps.  Every branch here is on compile-time values, so the unrolled
 // body is straight-line code (a run-time branch inside it lets the compiler sink the
 // math below it and keep every fragment of the slab live at once).
-//   BODY_MAIN: issue slab kt+S-1 at the first k-step; at the last k-step wait for slab
-//              kt+1 leaving S-2 slabs in flight, barrier, read slab kt+1's first fragments.
+//   BODY_MAIN: the copy of slab kt+S-1 is issued in CS parts over the first CS k-steps
+//              (a burst of copies stalls the wave's instruction issue and with it the
+//              math); at the last k-step wait for slab kt+1 leaving S-2 slabs in flight,
+//              barrier, read slab kt+1's first fragments.
 //   BODY_TAIL: no slab left to issue; wait for everything issued (<= S-2 slabs, the
 //              tail of the K loop), barrier, read slab kt+1's first fragments.
 //   BODY_LAST: the last slab: no copy, no barrier, no read-ahead.
-template <int S, int KS, int BODY, class Ops>
+template <int S, int KS, int CS, int BODY, class Ops>
 GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot) {
+    static_assert(CS >= 1 && CS < KS, "copies are issued before the last k-step's wait");
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        if (BODY == BODY_MAIN && ks == 0) ops.issue(kt + S - 1, issue_slot);
+        if (BODY == BODY_MAIN && ks < CS) ops.issue(kt + S - 1, issue_slot, ks, CS);
         if (ks == KS - 1) {
             if (BODY != BODY_LAST) {
                 ops.wait_lds();
@@ -72,8 +75,13 @@ GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot
             if (ks % 2 == 0) ops.template frag<1>(kt, slot, ks + 1);
             else ops.template frag<0>(kt, slot, ks + 1);
         }
-        if (ks % 2 == 0) ops.template math<0>(ks);
-        else ops.template math<1>(ks);
+        if (BODY == BODY_MAIN && ks < CS) {
+            if (ks % 2 == 0) ops.template math<0, CS>(ks);
+            else ops.template math<1, CS>(ks);
+        } else {
+            if (ks % 2 == 0) ops.template math<0, 0>(ks);
+            else ops.template math<1, 0>(ks);
+        }
     }
 }
 
@@ -87,20 +95,21 @@ GEMM_HD void single_slab_compute(Ops& ops, int kt) {
             if (ks % 2 == 0) ops.template frag<1>(kt, 0, ks + 1);
             else ops.template frag<0>(kt, 0, ks + 1);
         }
-        if (ks % 2 == 0) ops.template math<0>(ks);
-        else ops.template math<1>(ks);
+        if (ks % 2 == 0) ops.template math<0, 0>(ks);
+        else ops.template math<1, 0>(ks);
     }
 }
 
-// Direct global->LDS ring.  KS = k-steps per slab (even).
-template <int S, int KS, class Ops>
+// Direct global->LDS ring.  KS = k-steps per slab (even); CS = k-steps over which the
+// copy of one slab is spread.
+template <int S, int KS, int CS, class Ops>
 GEMM_HD void ring_mainloop(Ops& ops, int numK) {
     static_assert(KS % 2 == 0, "fragment double-buffering needs an even number of k-steps");
     static_assert(S >= 1, "at least one LDS slot");
     if (numK <= 0) return;
     if constexpr (S == 1) {
         for (int kt = 0; kt < numK; ++kt) {
-            ops.issue(kt, 0);
+            ops.issue(kt, 0, 0, 1);
             ops.template wait_slabs<0>();
             ops.barrier();
             single_slab_compute<KS>(ops, kt);
@@ -110,7 +119,7 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
     } else {
         // prologue: slabs 0 .. S-2 (fewer if K is short); wait for slab 0
         for (int s = 0; s < S - 1; ++s)
-            if (s < numK) ops.issue(s, s);
+            if (s < numK) ops.issue(s, s, 0, 1);
         if (numK >= S - 1) ops.template wait_slabs<S - 2>();
         else ops.template wait_slabs<0>();
         ops.barrier();
@@ -121,16 +130,16 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
         const int main_end = numK - S + 1;  // slabs whose body still issues a copy
         for (; kt < main_end; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
+            ring_slab<S, KS, CS, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
             slot = next_slot;
             issue_slot = (issue_slot + 1 == S) ? 0 : issue_slot + 1;
         }
         for (; kt < numK - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, BODY_TAIL>(ops, kt, slot, 0, next_slot);
+            ring_slab<S, KS, CS, BODY_TAIL>(ops, kt, slot, 0, next_slot);
             slot = next_slot;
         }
-        ring_slab<S, KS, BODY_LAST>(ops, kt, slot, 0, 0);
+        ring_slab<S, KS, CS, BODY_LAST>(ops, kt, slot, 0, 0);
     }
 }
 
@@ -152,8 +161,8 @@ GEMM_HD void staged_slab(Ops& ops, int kt, int slot) {
             if (ks % 2 == 0) ops.template frag<1>(kt, slot, ks + 1);
             else ops.template frag<0>(kt, slot, ks + 1);
         }
-        if (ks % 2 == 0) ops.template math<0>(ks);
-        else ops.template math<1>(ks);
+        if (ks % 2 == 0) ops.template math<0, 0>(ks);
+        else ops.template math<1, 0>(ks);
     }
 }
 
