@@ -157,10 +157,10 @@ gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
  *   5 WRITE    staged kernels: registers of slab `slab` -> ring slot `slot`
  *   6 WAIT_LDS the wave's own LDS reads and writes have completed
  * kernel: GEMM_KERNEL_VALU_RING / MFMA_RING / VALU_STAGED / MFMA_STAGED; ksteps = k-steps
- * per slab (2, 4 or 8), plus 16*(c-1) for a ring kernel that spreads the copy of a slab
- * over c k-steps (c = 1..3, c < k-steps): its ISSUE events then carry
- * arg = part | (c << 8).  Returns the number of events (writes at most `capacity` of
- * them), or -1 for bad arguments. */
+ * per slab (2, 4 or 8), plus 16 for a ring kernel that spreads the copy of each slab
+ * over the k-steps (one part per k-step; its ISSUE events carry arg = part | (parts << 8)).
+ * Returns the number of events (writes at most `capacity` of them), or -1 for bad
+ * arguments. */
 int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity);
 
 const char* gemm_status_string(gemm_status_t status);

@@ -84,10 +84,10 @@ def simulate(events, S, numK, ksteps, staged):
 
 @pytest.mark.parametrize("kernel", [lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("ksteps,cs", [(2, 1), (4, 1), (8, 1), (4, 2), (4, 3), (8, 3)])
-def test_ring_protocol(kernel, S, ksteps, cs):
+@pytest.mark.parametrize("ksteps,spread", [(2, 0), (4, 0), (8, 0), (2, 1), (4, 1), (8, 1)])
+def test_ring_protocol(kernel, S, ksteps, spread):
     for numK in list(range(0, 12)) + [33, 40]:
-        ev = lg.gemm_schedule(kernel, S, numK, ksteps + 16 * (cs - 1))
+        ev = lg.gemm_schedule(kernel, S, numK, ksteps + 16 * spread)
         assert ev is not None
         barriers, waits = simulate(ev, S, numK, ksteps, staged=False)
         if numK == 0:
@@ -143,7 +143,7 @@ def test_bad_arguments():
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 6, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 3, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 3) is None
-    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 2 + 16) is None      # 2 copy steps, 2 k-steps
+    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 2 + 32) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 2, 4, 4 + 16) is None
     assert lg.gemm_schedule(99, 2, 4, 4) is None
 

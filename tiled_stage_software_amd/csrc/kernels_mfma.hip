@@ -90,11 +90,11 @@ struct MfmaCompute {
             fb[BUF][j] = *reinterpret_cast<LDS_AS const frag_t*>(st + b_off[ks] + j * 32 * ROWB);
     }
 
-    // The MFMAs of one k-step.  COPIES global->LDS copies and the next k-step's TM+TN
-    // fragment reads were issued in program order just before; the scheduling groups
-    // interleave them with the first MFMAs (one fragment read and COPIES/(TM+TN) copies
-    // after each MFMA) so that their latency runs under the remaining MFMAs instead of
-    // stalling the next k-step.
+    // The MFMAs of one k-step.  The next k-step's TM+TN fragment reads and COPIES
+    // global->LDS copies were issued in program order just before; the scheduling groups
+    // place one fragment read after each of the first TM+TN MFMAs and the copies evenly
+    // among all the MFMAs, so that their latency runs under the remaining MFMAs and the
+    // copies reach the texture path at the rate it drains them.
     template <int BUF, int COPIES>
     __device__ __forceinline__ void math() {
 #pragma unroll
@@ -103,15 +103,16 @@ struct MfmaCompute {
             for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(fb[BUF][j], fa[BUF][i], acc[i][j]);
         constexpr int NF = TM + TN;
         constexpr int NM = TM * TN;
-        constexpr int CPM = (COPIES + NF - 1) / NF;
         static_assert(NM >= NF, "at least one MFMA per fragment read");
+        constexpr int STRIDE = COPIES > 0 ? (NM / COPIES > 0 ? NM / COPIES : 1) : NM + 1;
+        constexpr int PER = COPIES > NM ? (COPIES + NM - 1) / NM : 1;
 #pragma unroll
-        for (int i = 0; i < NF; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
-            if constexpr (CPM > 0) __builtin_amdgcn_sched_group_barrier(0x020, CPM, 0);  // VMEM read
+        for (int i = 0; i < NM; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
+            if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
+            if (COPIES > 0 && i % STRIDE == 0 && (i / STRIDE) * PER < COPIES)
+                __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);            // VMEM read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NM - NF, 0);
         // keep the k-step structure: nothing of the next k-step is hoisted above here
         __builtin_amdgcn_sched_barrier(0);
     }
@@ -171,11 +172,12 @@ struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF, int CS>
-    __device__ __forceinline__ void math(int) { C::template math<BUF, CS ? (L + CS - 1) / CS : 0>(); }
+    // HAS: this k-step issued one part of PARTS of a slab copy (L copies per slab).
+    template <int BUF, int HAS, int PARTS>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, HAS ? (L + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int CS>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
     occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, (BM / WM) * (BN / WN) > 64 * 64 ? 1 : 2))))
 void mfma_ring_kernel(const GemmParams p) {
@@ -192,7 +194,7 @@ void mfma_ring_kernel(const GemmParams p) {
     ops.init((LDS_AS char*)(smem_raw));
     ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
     ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-    gemm_sched::ring_mainloop<S, Ops::KS, CS>(ops, p.K / BK);
+    gemm_sched::ring_mainloop<S, Ops::KS, SPREAD>(ops, p.K / BK);
     ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
 }
 
@@ -219,7 +221,7 @@ struct MfmaStagedOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
     __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
-    template <int BUF, int COPIES>
+    template <int BUF, int HAS, int PARTS>
     __device__ __forceinline__ void math(int) { C::template math<BUF, 0>(); }
 };
 
@@ -242,10 +244,10 @@ void mfma_staged_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------- launch tables
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int CS = 1>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, CS>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
@@ -282,25 +284,26 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3>(p, st);
             if (S == 4) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 4>(p, st);
             break;
-        case 4:  // 256x256x64, copies of a slab spread over 2 k-steps
-            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, 2>(p, st);
+        case 4:  // 256x256x64, 2x2 waves, copies spread over the whole slab
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, true>(p, st);
             break;
-        case 5:  // 256x256x64, copies spread over 3 k-steps
-            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, 3>(p, st);
+        case 5:  // 256x256x32, 2x2 waves, copies spread
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 3, true>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 4, true>(p, st);
             break;
-        case 6:  // 128x128x64, copies spread over 2 k-steps
-            if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2, 2>(p, st);
-            if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, 2>(p, st);
+        case 6:  // 128x128x64, copies spread
+            if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2, true>(p, st);
+            if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, true>(p, st);
             break;
-        case 7:  // 256x256x64, 2x4 waves of 128x64 (two waves per SIMD)
-            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 4, 2>(p, st);
+        case 7:  // 256x256x64, 2x4 waves of 128x64 (two waves per SIMD), copies spread
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 4, 2, true>(p, st);
             break;
         case 8:  // 256x256x64, 4x2 waves of 64x128 (two waves per SIMD)
             if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 4, 2, 2>(p, st);
             break;
-        case 9:  // 256x256x32, 2x4 waves of 128x64, deeper ring
-            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3>(p, st);
-            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4>(p, st);
+        case 9:  // 256x256x32, 2x4 waves of 128x64, deeper ring, copies spread
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4, true>(p, st);
             break;
     }
     return hipErrorInvalidValue;

@@ -51,12 +51,12 @@ const Tile kMfmaRing[] = {
     {1, 256, 256, 64, 256, S1 | S2, 2, (256 + 256) * 64 * 2},
     {2, 256, 256, 32, 256, S1 | S2 | S3 | S4, 3, (256 + 256) * 32 * 2},
     {3, 128, 128, 64, 256, S1 | S2 | S3 | S4, 2, (128 + 128) * 64 * 2},
-    {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies over 2 k-steps
-    {5, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies over 3 k-steps
-    {6, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},     // copies over 2 k-steps
-    {7, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves, 128x64 each
-    {8, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves, 64x128 each
-    {9, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},     // 8 waves, BK 32
+    {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies spread over the slab
+    {5, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},     // copies spread
+    {6, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},     // copies spread
+    {7, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves 128x64, spread
+    {8, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves 64x128
+    {9, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},     // 8 waves, BK 32, spread
 };
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
@@ -268,7 +268,7 @@ struct Recorder {
     template <int N> void wait_slabs() { push(2, -1, -1, N); }
     void barrier() { push(3, -1, -1, 0); }
     template <int BUF> void frag(int slab, int slot, int ks) { push(4, slab, slot, ks); }
-    template <int BUF, int COPIES> void math(int) {}
+    template <int BUF, int HAS, int PARTS> void math(int) {}
     void wait_lds() { push(6, -1, -1, 0); }
     void issue(int slab, int slot, int part, int parts) { push(1, slab, slot, part | (parts << 8)); }
     void load(int slab) { push(1, slab, -1, 0); }
@@ -276,26 +276,23 @@ struct Recorder {
 };
 
 template <int S, int KS>
-void rec_ring(Recorder& r, int numK, int cs) {
-    if (cs == 1) gemm_sched::ring_mainloop<S, KS, 1>(r, numK);
-    else if constexpr (KS > 2) {
-        if (cs == 2) gemm_sched::ring_mainloop<S, KS, 2>(r, numK);
-        else if (cs == 3) gemm_sched::ring_mainloop<S, KS, 3>(r, numK);
-    }
+void rec_ring(Recorder& r, int numK, int spread) {
+    if (spread) gemm_sched::ring_mainloop<S, KS, true>(r, numK);
+    else gemm_sched::ring_mainloop<S, KS, false>(r, numK);
 }
 template <int S, int KS>
 void rec_staged(Recorder& r, int numK) { gemm_sched::staged_mainloop<S, KS>(r, numK); }
 
 template <int S>
-bool rec_ring_ks(Recorder& r, int ks, int numK, int cs) {
-    if (cs < 1 || cs >= ks || cs > 3) return false;
+bool rec_ring_ks(Recorder& r, int ks, int numK, int spread) {
     switch (ks) {
-        case 2: rec_ring<S, 2>(r, numK, cs); return true;
-        case 4: rec_ring<S, 4>(r, numK, cs); return true;
-        case 8: rec_ring<S, 8>(r, numK, cs); return true;
+        case 2: rec_ring<S, 2>(r, numK, spread); return true;
+        case 4: rec_ring<S, 4>(r, numK, spread); return true;
+        case 8: rec_ring<S, 8>(r, numK, spread); return true;
     }
     return false;
 }
+
 template <int S>
 bool rec_staged_ks(Recorder& r, int ks, int numK) {
     switch (ks) {
@@ -378,9 +375,10 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
     if (num_k < 0 || capacity < 0 || (capacity > 0 && !events)) return -1;
     Recorder r;
     bool ok = false;
-    // ksteps = k-steps per slab + 16 * (copy steps - 1) for ring kernels
-    const int cs = 1 + (ksteps >> 4);
+    // ksteps = k-steps per slab, + 16 for a ring kernel that spreads each copy over the slab
+    const int cs = ksteps >> 4;
     ksteps &= 15;
+    if (cs > 1) return -1;
     if (kernel == GEMM_KERNEL_VALU_RING || kernel == GEMM_KERNEL_MFMA_RING) {
         switch (nstage) {
             case 1: ok = rec_ring_ks<1>(r, ksteps, num_k, cs); break;
@@ -390,7 +388,7 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
             case 5: ok = rec_ring_ks<5>(r, ksteps, num_k, cs); break;
         }
     } else if (kernel == GEMM_KERNEL_VALU_STAGED || kernel == GEMM_KERNEL_MFMA_STAGED) {
-        if (cs != 1) return -1;
+        if (cs != 0) return -1;
         switch (nstage) {
             case 1: ok = rec_staged_ks<1>(r, ksteps, num_k); break;
             case 2: ok = rec_staged_ks<2>(r, ksteps, num_k); break;

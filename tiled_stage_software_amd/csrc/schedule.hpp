@@ -46,41 +46,56 @@ namespace gemm_sched {
 GEMM_HD constexpr int imin(int a, int b) { return a < b ? a : b; }
 GEMM_HD constexpr int imax(int a, int b) { return a > b ? a : b; }
 
-enum { BODY_MAIN = 0, BODY_TAIL = 1, BODY_LAST = 2 };
+enum { BODY_MAIN = 0, BODY_MAIN_END = 1, BODY_TAIL = 2, BODY_LAST = 3 };
 
 // One slab of KS k-steps.  Every branch here is on compile-time values, so the unrolled
 // body is straight-line code (a run-time branch inside it lets the compiler sink the
 // math below it and keep every fragment of the slab live at once).
-//   BODY_MAIN: the copy of slab kt+S-1 is issued in CS parts over the first CS k-steps
-//              (a burst of copies stalls the wave's instruction issue and with it the
-//              math); at the last k-step wait for slab kt+1 leaving S-2 slabs in flight,
-//              barrier, read slab kt+1's first fragments.
-//   BODY_TAIL: no slab left to issue; wait for everything issued (<= S-2 slabs, the
-//              tail of the K loop), barrier, read slab kt+1's first fragments.
-//   BODY_LAST: the last slab: no copy, no barrier, no read-ahead.
-template <int S, int KS, int CS, int BODY, class Ops>
+//
+// SPREAD = false: the whole copy of slab kt+S-1 is issued at the first k-step.
+// SPREAD = true:  the copy is split into KS parts, one per k-step: part 0 right after
+//   the barrier that ends slab kt-1 (that barrier frees the slot), parts 1..KS-1 at
+//   k-steps 0..KS-2 of slab kt.  The copies then trickle out at the rate the texture
+//   path drains them instead of backing up the wave's issue, and every part is still
+//   issued before the wait that counts it.
+//   BODY_MAIN:     issues (its parts of) slab kt+S-1 and, with SPREAD, part 0 of slab
+//                  kt+S after its barrier; waits for slab kt+1 leaving S-2 slabs in flight.
+//   BODY_MAIN_END: the last slab that issues: no part 0 of a next slab.
+//   BODY_TAIL:     nothing left to issue; waits for everything in flight.
+//   BODY_LAST:     the last slab: no copy, no barrier, no read-ahead.
+template <int S, int KS, bool SPREAD, int BODY, class Ops>
 GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot) {
-    static_assert(CS >= 1 && CS < KS, "copies are issued before the last k-step's wait");
+    constexpr bool ISSUING = BODY == BODY_MAIN || BODY == BODY_MAIN_END;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
-        if (BODY == BODY_MAIN && ks < CS) ops.issue(kt + S - 1, issue_slot, ks, CS);
+        int copies_here = 0;  // parts issued in this k-step (for the math's interleave)
+        if (ISSUING) {
+            if (!SPREAD && ks == 0) { ops.issue(kt + S - 1, issue_slot, 0, 1); copies_here = KS; }
+            if (SPREAD && ks < KS - 1) { ops.issue(kt + S - 1, issue_slot, ks + 1, KS); copies_here = 1; }
+        }
         if (ks == KS - 1) {
             if (BODY != BODY_LAST) {
                 ops.wait_lds();
-                ops.template wait_slabs<BODY == BODY_MAIN ? S - 2 : 0>();
+                ops.template wait_slabs<BODY == BODY_TAIL ? 0 : S - 2>();
                 ops.barrier();
                 ops.template frag<0>(kt + 1, next_slot, 0);
+                // the barrier freed this slab's slot: start the copy of slab kt+S into it
+                if (SPREAD && BODY == BODY_MAIN) { ops.issue(kt + S, slot, 0, KS); copies_here = 1; }
             }
         } else {
             if (ks % 2 == 0) ops.template frag<1>(kt, slot, ks + 1);
             else ops.template frag<0>(kt, slot, ks + 1);
         }
-        if (BODY == BODY_MAIN && ks < CS) {
-            if (ks % 2 == 0) ops.template math<0, CS>(ks);
-            else ops.template math<1, CS>(ks);
+        // copies_here is a compile-time constant after unrolling
+        if (copies_here == KS) {
+            if (ks % 2 == 0) ops.template math<0, 1, 1>(ks);
+            else ops.template math<1, 1, 1>(ks);
+        } else if (copies_here == 1) {
+            if (ks % 2 == 0) ops.template math<0, 1, KS>(ks);
+            else ops.template math<1, 1, KS>(ks);
         } else {
-            if (ks % 2 == 0) ops.template math<0, 0>(ks);
-            else ops.template math<1, 0>(ks);
+            if (ks % 2 == 0) ops.template math<0, 0, 1>(ks);
+            else ops.template math<1, 0, 1>(ks);
         }
     }
 }
@@ -95,14 +110,13 @@ GEMM_HD void single_slab_compute(Ops& ops, int kt) {
             if (ks % 2 == 0) ops.template frag<1>(kt, 0, ks + 1);
             else ops.template frag<0>(kt, 0, ks + 1);
         }
-        if (ks % 2 == 0) ops.template math<0, 0>(ks);
-        else ops.template math<1, 0>(ks);
+        if (ks % 2 == 0) ops.template math<0, 0, 1>(ks);
+        else ops.template math<1, 0, 1>(ks);
     }
 }
 
-// Direct global->LDS ring.  KS = k-steps per slab (even); CS = k-steps over which the
-// copy of one slab is spread.
-template <int S, int KS, int CS, class Ops>
+// Direct global->LDS ring.  KS = k-steps per slab (even); SPREAD: see ring_slab.
+template <int S, int KS, bool SPREAD, class Ops>
 GEMM_HD void ring_mainloop(Ops& ops, int numK) {
     static_assert(KS % 2 == 0, "fragment double-buffering needs an even number of k-steps");
     static_assert(S >= 1, "at least one LDS slot");
@@ -124,22 +138,30 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
         else ops.template wait_slabs<0>();
         ops.barrier();
         ops.template frag<0>(0, 0, 0);
+        // SPREAD: part 0 of slab S-1 goes into the still unused slot S-1
+        if (SPREAD && numK > S - 1) ops.issue(S - 1, S - 1, 0, KS);
         int kt = 0;
         int slot = 0;            // slot of slab kt
         int issue_slot = S - 1;  // slot of slab kt+S-1 (= the slot slab kt-1 used)
         const int main_end = numK - S + 1;  // slabs whose body still issues a copy
-        for (; kt < main_end; ++kt) {
+        for (; kt < main_end - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, CS, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
+            ring_slab<S, KS, SPREAD, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
             slot = next_slot;
             issue_slot = (issue_slot + 1 == S) ? 0 : issue_slot + 1;
         }
+        if (kt < main_end) {
+            const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
+            ring_slab<S, KS, SPREAD, BODY_MAIN_END>(ops, kt, slot, issue_slot, next_slot);
+            slot = next_slot;
+            ++kt;
+        }
         for (; kt < numK - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, CS, BODY_TAIL>(ops, kt, slot, 0, next_slot);
+            ring_slab<S, KS, SPREAD, BODY_TAIL>(ops, kt, slot, 0, next_slot);
             slot = next_slot;
         }
-        ring_slab<S, KS, CS, BODY_LAST>(ops, kt, slot, 0, 0);
+        ring_slab<S, KS, SPREAD, BODY_LAST>(ops, kt, slot, 0, 0);
     }
 }
 
@@ -161,8 +183,8 @@ GEMM_HD void staged_slab(Ops& ops, int kt, int slot) {
             if (ks % 2 == 0) ops.template frag<1>(kt, slot, ks + 1);
             else ops.template frag<0>(kt, slot, ks + 1);
         }
-        if (ks % 2 == 0) ops.template math<0, 0>(ks);
-        else ops.template math<1, 0>(ks);
+        if (ks % 2 == 0) ops.template math<0, 0, 1>(ks);
+        else ops.template math<1, 0, 1>(ks);
     }
 }
 
