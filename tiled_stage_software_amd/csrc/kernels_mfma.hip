@@ -1,56 +1,86 @@
-// kernels_mfma.hip -- bf16 / f16 GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16).
+// kernels_mfma.hip -- bf16 / f16 GEMM on the CDNA4 matrix cores (v_mfma_f32_32x32x16 or
+// v_mfma_f32_16x16x32).
 //
 // Hierarchy (sections 1-3 of "CUTLASS-Cute 初步(6)：CUDA GEMM 计算优化、Multi-Stage 与软流水"):
 //   workgroup tile BM x BN of C, looped over K in slabs of BK;
 //   WM x WN waves, each owning a disjoint (BM/WM) x (BN/WN) block of accumulators;
-//   per wave and per 16-deep k-step, (BM/WM/32) A fragments and (BN/WN/32) B fragments
-//   are read from LDS and combined by 32x32x16 MFMAs -- waves in one row of the tile
-//   read the same A fragments, waves in one column the same B fragments.
+//   per wave and per k-step (16 deep for 32x32x16, 32 deep for 16x16x32), (BM/WM/MI) A
+//   fragments and (BN/WN/MI) B fragments are read from LDS and combined by MI x MI
+//   MFMAs -- waves in one row of the tile read the same A fragments, waves in one column
+//   the same B fragments.
 //
 // Operand fragments (one 16-byte LDS read per lane): lane l holds 8 consecutive k of
-// row (l mod 32) of the 32-row block, k-chunk l/32 of the k-step.  The MFMA is fed
-// (B fragment, A fragment), so the 32x32 result it returns is C transposed: lane l,
-// register 4g+j holds C[m = l mod 32][n = 8g + 4*(l/32) + j], i.e. 4 consecutive columns
-// per lane and register group, which the epilogue stores as one vector.
+// row (l mod MI) of the MI-row block, k-chunk l/MI of the k-step; A and B lanes of one
+// lane group carry the same k, so each product term meets its partner.  The MFMA is fed
+// (B fragment, A fragment), so the MI x MI result it returns is C transposed: for
+// MI = 32, lane l, register 4g+j holds C[m = l mod 32][n = 8g + 4*(l/32) + j]; for
+// MI = 16, lane l, register j holds C[m = l mod 16][n = 4*(l/16) + j] -- 4 consecutive
+// columns per lane and register group, which the epilogue stores as one vector.
 #include "common.hpp"
 #include "loaders.hpp"
 #include "launch.hpp"
 
 namespace gemm {
 
-template <typename T>
+// MI x MI x KI matrix instruction: MI = 32 (32x32x16, 16 f32 results per lane) or
+// MI = 16 (16x16x32, 4 f32 results per lane); both take 8 16-bit values per lane and
+// operand and run at the same peak rate.
+template <typename T, int MI>
 struct Mfma;
 template <>
-struct Mfma<__bf16> {
+struct Mfma<__bf16, 32> {
     typedef bf16x8 frag;
-    static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    typedef f32x16 acc;
+    static __device__ __forceinline__ acc run(frag a, frag b, acc c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
     }
 };
 template <>
-struct Mfma<_Float16> {
+struct Mfma<_Float16, 32> {
     typedef f16x8 frag;
-    static __device__ __forceinline__ f32x16 run(frag a, frag b, f32x16 c) {
+    typedef f32x16 acc;
+    static __device__ __forceinline__ acc run(frag a, frag b, acc c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<__bf16, 16> {
+    typedef bf16x8 frag;
+    typedef f32x4 acc;
+    static __device__ __forceinline__ acc run(frag a, frag b, acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+template <>
+struct Mfma<_Float16, 16> {
+    typedef f16x8 frag;
+    typedef f32x4 acc;
+    static __device__ __forceinline__ acc run(frag a, frag b, acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
     }
 };
 
 // Shared compute state: accumulators and double-buffered fragments of one wave.
-template <typename T, int BM, int BN, int BK, int WM, int WN>
+template <typename T, int BM, int BN, int BK, int WM, int WN, int MI = 32>
 struct MfmaCompute {
     static constexpr int ROWB = BK * 2;
     static constexpr int CPR = ROWB / 16;
     static constexpr int WTM = BM / WM, WTN = BN / WN;
-    static constexpr int TM = WTM / 32, TN = WTN / 32;
-    static constexpr int KS = BK / 16;
+    static constexpr int TM = WTM / MI, TN = WTN / MI;
+    static constexpr int KI = 512 / MI;             // k per instruction: 16 or 32
+    static constexpr int LG = 64 / MI;              // lane groups = 16-byte k-chunks per k-step
+    static constexpr int NR = MI * MI / 64;         // f32 results per lane and instruction
+    static constexpr int KS = BK / KI;
     static constexpr int A_BYTES = BM * ROWB;
     static constexpr int B_BYTES = BN * ROWB;
     static constexpr int STAGE = A_BYTES + B_BYTES;
-    static_assert(BK % 32 == 0, "two 16-deep k-steps per slab at least");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile is made of 32x32 blocks");
+    static_assert(MI == 16 || MI == 32, "instruction shape");
+    static_assert(BK % (2 * KI) == 0, "two k-steps per slab at least");
+    static_assert(WTM % MI == 0 && WTN % MI == 0, "wave tile is made of MI x MI blocks");
 
-    typedef typename Mfma<T>::frag frag_t;
-    f32x16 acc[TM][TN];
+    typedef typename Mfma<T, MI>::frag frag_t;
+    typedef typename Mfma<T, MI>::acc acc_t;
+    acc_t acc[TM][TN];
     frag_t fa[2][TM];
     frag_t fb[2][TN];
     uint32_t a_off[KS];  // per lane LDS byte offsets within a stage (wave tile row 0)
@@ -62,12 +92,12 @@ struct MfmaCompute {
         const int w = wave_id();
         const int wm = w / WN, wn = w % WN;
         const int lane = lane_id();
-        const int r = lane & 31;
-        const int hi = lane >> 5;
+        const int r = lane % MI;
+        const int g = lane / MI;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c = 2 * ks + hi;
-            const int sw = c ^ swz<CPR>(r);  // wave-tile rows are multiples of 32: swz period 16
+            const int c = LG * ks + g;
+            const int sw = c ^ swz<CPR>(r);  // wave-tile rows are multiples of 16: swz period 16
             a_off[ks] = (uint32_t)((wm * WTM + r) * ROWB + (sw << 4));
             b_off[ks] = (uint32_t)(A_BYTES + (wn * WTN + r) * ROWB + (sw << 4));
         }
@@ -76,7 +106,7 @@ struct MfmaCompute {
 #pragma unroll
             for (int j = 0; j < TN; ++j)
 #pragma unroll
-                for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+                for (int e = 0; e < NR; ++e) acc[i][j][e] = 0.0f;
     }
 
     template <int BUF>
@@ -84,10 +114,10 @@ struct MfmaCompute {
         LDS_AS const char* st = smem + slot * STAGE;
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            fa[BUF][i] = *reinterpret_cast<LDS_AS const frag_t*>(st + a_off[ks] + i * 32 * ROWB);
+            fa[BUF][i] = *reinterpret_cast<LDS_AS const frag_t*>(st + a_off[ks] + i * MI * ROWB);
 #pragma unroll
         for (int j = 0; j < TN; ++j)
-            fb[BUF][j] = *reinterpret_cast<LDS_AS const frag_t*>(st + b_off[ks] + j * 32 * ROWB);
+            fb[BUF][j] = *reinterpret_cast<LDS_AS const frag_t*>(st + b_off[ks] + j * MI * ROWB);
     }
 
     // The MFMAs of one k-step.  The next k-step's TM+TN fragment reads and COPIES
@@ -100,7 +130,7 @@ struct MfmaCompute {
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T>::run(fb[BUF][j], fa[BUF][i], acc[i][j]);
+            for (int j = 0; j < TN; ++j) acc[i][j] = Mfma<T, MI>::run(fb[BUF][j], fa[BUF][i], acc[i][j]);
         constexpr int NF = TM + TN;
         constexpr int NM = TM * TN;
         static_assert(NM >= NF, "at least one MFMA per fragment read");
@@ -127,13 +157,15 @@ struct MfmaCompute {
         const int lane = lane_id();
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
-            const int m = m0 + wm * WTM + i * 32 + (lane & 31);
+            const int m = m0 + wm * WTM + i * MI + (lane % MI);
             const bool mok = m >= m_keep && m < p.M;
 #pragma unroll
             for (int j = 0; j < TN; ++j) {
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int n = n0 + wn * WTN + j * 32 + g * 8 + (lane >> 5) * 4;
+                for (int g = 0; g < NR / 4; ++g) {
+                    // MI = 32: register group g covers n = 8g + 4*(lane/32) + 0..3;
+                    // MI = 16: the single group covers n = 4*(lane/16) + 0..3
+                    const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
                     if (mok && n >= n_keep && n < p.N) {
                         f32x4 v;
                         v[0] = acc[i][j][4 * g + 0];
@@ -149,9 +181,9 @@ struct MfmaCompute {
 };
 
 // ---------------------------------------------------------------- direct ring kernel
-template <typename T, int BM, int BN, int BK, int WM, int WN, int S>
-struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
-    typedef MfmaCompute<T, BM, BN, BK, WM, WN> C;
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int MI>
+struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN, MI> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN, MI> C;
     static constexpr int NW = WM * WN;
     DirectLoader<BM, C::ROWB, NW, true> la;
     DirectLoader<BN, C::ROWB, NW, true> lb;
@@ -177,11 +209,11 @@ struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void math(int) { C::template math<BUF, HAS ? (L + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD, int MI>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
     occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, (BM / WM) * (BN / WN) > 64 * 64 ? 1 : 2))))
 void mfma_ring_kernel(const GemmParams p) {
-    typedef MfmaRingOps<T, BM, BN, BK, WM, WN, S> Ops;
+    typedef MfmaRingOps<T, BM, BN, BK, WM, WN, S, MI> Ops;
     __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -244,10 +276,10 @@ void mfma_staged_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------- launch tables
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false, int MI = 32>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD, MI>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
@@ -304,6 +336,16 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
         case 9:  // 256x256x32, 2x4 waves of 128x64, deeper ring, copies spread
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true>(p, st);
             if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4, true>(p, st);
+            break;
+        case 10:  // 256x256x64, 2x2 waves, 16x16x32 instructions
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, false, 16>(p, st);
+            break;
+        case 11:  // 256x256x64, 2x2 waves, 16x16x32 instructions, copies spread
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, true, 16>(p, st);
+            break;
+        case 12:  // 128x128x64, 2x2 waves, 16x16x32 instructions
+            if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2, false, 16>(p, st);
+            if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, false, 16>(p, st);
             break;
     }
     return hipErrorInvalidValue;

@@ -57,6 +57,9 @@ const Tile kMfmaRing[] = {
     {7, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves 128x64, spread
     {8, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},          // 8 waves 64x128
     {9, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},     // 8 waves, BK 32, spread
+    {10, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32 instructions
+    {11, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32, spread
+    {12, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},    // 16x16x32
 };
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
