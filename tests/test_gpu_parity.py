@@ -358,7 +358,7 @@ def _planned_variants():
     out = []
     for kern, dt, la, lb in ((K_MFMA_RING, "bf16", ROW, COL), (K_MFMA_STAGED, "f16", ROW, ROW),
                              (K_VALU_RING, "f32", ROW, ROW), (K_VALU_STAGED, "f32", COL, ROW)):
-        for tile in range(1, 13):
+        for tile in range(1, 21):
             for S in range(1, 6):
                 code = {"f32": 0, "bf16": 1, "f16": 2}[dt]
                 M, N, K = 512, 512, 384

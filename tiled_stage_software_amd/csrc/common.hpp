@@ -71,13 +71,6 @@ constexpr int occupancy_waves(int threads, int lds_bytes, int cap) {
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
-// ---------------------------------------------------------------- direct copies
-// 16 bytes per lane from global memory straight into LDS; the LDS destination of lane
-// i is lds_wave_base + 16*i (the base must be wave-uniform).
-__device__ __forceinline__ void copy16_to_lds(const void* g, LDS_AS void* lds_wave_base) {
-    __builtin_amdgcn_global_load_lds(g, lds_wave_base, 16, 0, 0);
-}
-
 // ---------------------------------------------------------------- LDS swizzle
 // 16-byte chunk c of LDS row r lives at chunk position c ^ swz(r).  For CPR = 8
 // (128-byte rows) and CPR = 4 (64-byte rows) the functions make any 8 or 16 consecutive

@@ -141,7 +141,7 @@ struct MfmaCompute {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                  // MFMA
             if (i < NF) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);      // DS read
             if (COPIES > 0 && i % STRIDE == 0 && (i / STRIDE) * PER < COPIES)
-                __builtin_amdgcn_sched_group_barrier(0x020, PER, 0);            // VMEM read
+                __builtin_amdgcn_sched_group_barrier(0x010, PER, 0);            // VMEM (the DMA copies)
         }
         // keep the k-step structure: nothing of the next k-step is hoisted above here
         __builtin_amdgcn_sched_barrier(0);
@@ -181,39 +181,113 @@ struct MfmaCompute {
 };
 
 // ---------------------------------------------------------------- direct ring kernel
-template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int MI>
+// PIN = false: fragment reads and copies are issued where the K-loop schedule asks for
+//   them and the compiler interleaves them with the MFMAs (scheduling-group hints).
+// PIN = true: frag() and issue() only note what is asked; the next math() issues it,
+//   one fragment read after each of the first TM+TN MFMAs and the k-step's copies evenly
+//   spaced over all its MFMAs, each MFMA group closed by a scheduling barrier so the
+//   order is exactly that.  Reads for the buffer math() is about to consume (the first
+//   k-step of the loop) are issued before its MFMAs; copies noted before a wait (the
+//   prologue) or before another request are issued at once.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int MI, bool PIN>
 struct MfmaRingOps : MfmaCompute<T, BM, BN, BK, WM, WN, MI> {
     typedef MfmaCompute<T, BM, BN, BK, WM, WN, MI> C;
     static constexpr int NW = WM * WN;
     DirectLoader<BM, C::ROWB, NW, true> la;
     DirectLoader<BN, C::ROWB, NW, true> lb;
-    static constexpr int L = DirectLoader<BM, C::ROWB, NW, true>::IPW + DirectLoader<BN, C::ROWB, NW, true>::IPW;
+    static constexpr int LA_N = DirectLoader<BM, C::ROWB, NW, true>::IPW;
+    static constexpr int L = LA_N + DirectLoader<BN, C::ROWB, NW, true>::IPW;
 
-    // Part `part` of `parts` of the copy of slab `slab` into ring slot `slot`: the L
-    // copies of this wave (A's first, then B's) are split into equal consecutive runs.
-    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
-        LDS_AS char* st = this->smem + slot * C::STAGE;
-        const int c0 = part * L / parts, c1 = (part + 1) * L / parts;
-        constexpr int LA_N = decltype(la)::IPW;
+    // deferred work (PIN): fragment LDS addresses per buffer, copy run [cp0, cp1)
+    LDS_AS const char* fpa[2];
+    LDS_AS const char* fpb[2];
+    bool fpend[2] = {false, false};
+    int cp_slab = 0, cp0 = 0, cp1 = 0;
+    LDS_AS char* cp_tile = nullptr;
+
+    // Copies [c0, c1) of this wave's L copies of slab `slab` (A's first, then B's).
+    __device__ __forceinline__ void copies(int slab, LDS_AS char* st, int c0, int c1) {
         la.issue(slab, st, c0, c1 < LA_N ? c1 : LA_N);
         lb.issue(slab, st + C::A_BYTES, c0 > LA_N ? c0 - LA_N : 0, c1 - LA_N);
     }
+    // Part `part` of `parts` of the copy of slab `slab` into ring slot `slot`: the L
+    // copies of this wave are split into equal consecutive runs.
+    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
+        LDS_AS char* st = this->smem + slot * C::STAGE;
+        const int c0 = part * L / parts, c1 = (part + 1) * L / parts;
+        if (PIN) {
+            flush();   // a second request before any math (the prologue): issue the first now
+            cp_slab = slab; cp_tile = st; cp0 = c0; cp1 = c1;
+        } else {
+            copies(slab, st, c0, c1);
+        }
+    }
+    // Issue noted copies that no math() took (before a wait that counts them).
+    __device__ __forceinline__ void flush() {
+        if (cp0 < cp1) copies(cp_slab, cp_tile, cp0, cp1);
+        cp0 = cp1 = 0;
+    }
     template <int N>
-    __device__ __forceinline__ void wait_slabs() { wait_vm<N * L>(); }
+    __device__ __forceinline__ void wait_slabs() {
+        if (PIN) flush();
+        wait_vm<N * L>();
+    }
     __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
     __device__ __forceinline__ void barrier() { gemm::barrier(); }
     template <int BUF>
-    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    __device__ __forceinline__ void frag(int, int slot, int ks) {
+        if (PIN) {
+            LDS_AS const char* st = this->smem + slot * C::STAGE;
+            fpa[BUF] = st + this->a_off[ks];
+            fpb[BUF] = st + this->b_off[ks];
+            fpend[BUF] = true;
+        } else {
+            C::template frag<BUF>(slot, ks);
+        }
+    }
+    template <int BUF>
+    __device__ __forceinline__ void read_now(int f) {
+        if (f < C::TM) this->fa[BUF][f] = *reinterpret_cast<LDS_AS const typename C::frag_t*>(fpa[BUF] + f * MI * C::ROWB);
+        else this->fb[BUF][f - C::TM] = *reinterpret_cast<LDS_AS const typename C::frag_t*>(fpb[BUF] + (f - C::TM) * MI * C::ROWB);
+    }
     // HAS: this k-step issued one part of PARTS of a slab copy (L copies per slab).
     template <int BUF, int HAS, int PARTS>
-    __device__ __forceinline__ void math(int) { C::template math<BUF, HAS ? (L + PARTS - 1) / PARTS : 0>(); }
+    __device__ __forceinline__ void math(int) {
+        if (!PIN) {
+            C::template math<BUF, HAS ? (L + PARTS - 1) / PARTS : 0>();
+            return;
+        }
+        constexpr int NB = BUF ^ 1;
+        constexpr int NM = C::TM * C::TN, NF = C::TM + C::TN;
+        constexpr int NC = HAS ? (L + PARTS - 1) / PARTS : 0;   // copies noted for this k-step (at most)
+        if (fpend[BUF]) {
+#pragma unroll
+            for (int f = 0; f < NF; ++f) read_now<BUF>(f);
+            fpend[BUF] = false;
+        }
+#pragma unroll
+        for (int t = 0; t < NM; ++t) {
+            const int i = t / C::TN, j = t % C::TN;
+            this->acc[i][j] = Mfma<T, MI>::run(this->fb[BUF][j], this->fa[BUF][i], this->acc[i][j]);
+            // the MFMA first: its operand wait must not also cover the reads issued next
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < NF && fpend[NB]) read_now<NB>(t);
+#pragma unroll
+            for (int q = 0; q < NC; ++q)
+                if (t == (q * NM) / NC + NM / (2 * NC) && cp0 + q < cp1) copies(cp_slab, cp_tile, cp0 + q, cp0 + q + 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        fpend[NB] = false;
+        if (cp0 + NC < cp1) copies(cp_slab, cp_tile, cp0 + NC, cp1);   // not reached by the schedule
+        cp0 = cp1 = 0;
+    }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD, int MI>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD, int MI, bool PIN>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(
     occupancy_waves(WM * WN * 64, S * MfmaCompute<T, BM, BN, BK, WM, WN>::STAGE, (BM / WM) * (BN / WN) > 64 * 64 ? 1 : 2))))
 void mfma_ring_kernel(const GemmParams p) {
-    typedef MfmaRingOps<T, BM, BN, BK, WM, WN, S, MI> Ops;
+    typedef MfmaRingOps<T, BM, BN, BK, WM, WN, S, MI, PIN> Ops;
     __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -276,10 +350,10 @@ void mfma_staged_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------- launch tables
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false, int MI = 32>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false, int MI = 32, bool PIN = false>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD, MI>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD, MI, PIN>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
     return hipGetLastError();
 }
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
@@ -346,6 +420,20 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
         case 12:  // 128x128x64, 2x2 waves, 16x16x32 instructions
             if (S == 2) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 2, false, 16>(p, st);
             if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, false, 16>(p, st);
+            break;
+        case 13:  // tile 1 with pinned issue order
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, false, 32, true>(p, st);
+            break;
+        case 14:  // tile 4 (spread) with pinned issue order
+            if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, true, 32, true>(p, st);
+            break;
+        case 15:  // tile 5 (256x256x32, spread) with pinned issue order
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 3, true, 32, true>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 4, true, 32, true>(p, st);
+            break;
+        case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
+            if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);
+            if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4, true, 32, true>(p, st);
             break;
     }
     return hipErrorInvalidValue;

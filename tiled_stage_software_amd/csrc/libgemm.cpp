@@ -60,6 +60,10 @@ const Tile kMfmaRing[] = {
     {10, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32 instructions
     {11, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32, spread
     {12, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},    // 16x16x32
+    {13, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 1, pinned issue order
+    {14, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 4, pinned
+    {15, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 5, pinned
+    {16, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 9, pinned
 };
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},

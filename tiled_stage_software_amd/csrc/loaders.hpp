@@ -6,7 +6,7 @@
 // multi-stage page, here as an XOR on 16-byte chunks so that the MFMA / FMA fragment
 // reads of consecutive rows spread over all LDS banks).
 //
-//  * DirectLoader: global_load_lds_dwordx4 -- each lane's 16 bytes go from HBM straight
+//  * DirectLoader: buffer_load_dwordx4 ... lds -- each lane's 16 bytes go from HBM straight
 //    into LDS without passing through registers (the role of the asynchronous copy of
 //    "Matrix multiplication" and of cp.async in the other pages).  The LDS destination
 //    of one wave instruction is 1 KiB contiguous, so the swizzle is produced by choosing
@@ -32,46 +32,79 @@ __device__ __forceinline__ int lds_offset(int r, int col) {
     return r * ROWB + (pc << 4) + (byte & 15);
 }
 
+// Word 3 of a raw (stride 0) buffer resource on gfx9-family parts: 32-bit data format,
+// no swizzle, no index stride.
+constexpr int kBufferFlags = 0x00020000;
+
 // ------------------------------------------------------------------------------------
 // LR rows of ROWB bytes, loaded by NW waves, IPW copies of 1 KiB per wave per slab.
+//
+// Wave w fills the contiguous band of LDS rows [w*IPW*RPI, (w+1)*IPW*RPI), copy i the
+// i-th KiB of that band.  The LDS destination of a DMA copy is M0 + the instruction's
+// immediate offset + 16*lane, and the same immediate is added to the global address;
+// so GROUP consecutive copies share one M0 value and step through the band with
+// immediates 0, 1 KiB, ..., the per-lane global offsets having that immediate taken
+// off in advance.  Rewriting M0 between DMA copies stalls the issuing wave, and the
+// wave is the one that feeds the matrix cores.
 template <int LR, int ROWB, int NW, bool SWZ>
 struct DirectLoader {
     static constexpr int CPR = ROWB / 16;
     static constexpr int RPI = 64 / CPR;            // LDS rows per copy instruction
     static constexpr int IPW = LR / (RPI * NW);     // copies per wave per slab
+    static constexpr int GROUP = 4;                 // copies per M0 value (immediates < 4 KiB)
     static_assert(ROWB % 16 == 0 && CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row bytes");
     static_assert(IPW >= 1 && IPW * RPI * NW == LR, "rows must split evenly over the waves");
-    static_assert(!SWZ || (RPI * NW) % 16 == 0, "swizzle must repeat between copies of a wave");
+    static_assert(RPI * ROWB == 1024, "one copy fills 1 KiB of LDS");
 
     const char* base;      // uniform: address of LDS row 0, chunk 0 of slab 0
     int64_t slab_step;     // uniform: bytes between consecutive slabs
-    uint32_t voff[IPW];    // per lane: global byte offset of this lane's chunk in copy i
-    int lds_wave;          // uniform: LDS byte offset of this wave's copy 0
+    uint32_t voff[IPW];    // per lane: global byte offset of its chunk in copy i, minus
+                           // the immediate that copy carries
+    int lds_wave;          // uniform: LDS byte offset of this wave's band
 
     // row_origin: global address of LDS row 0 / chunk 0 in slab 0; ld_bytes: bytes
-    // between consecutive LDS rows in global memory (the host keeps LR*ld_bytes < 2^31,
-    // so the per-lane offsets fit 32 bits and the copies use a scalar base + vector offset).
+    // between consecutive LDS rows in global memory (ld_bytes >= ROWB, and the host keeps
+    // LR*ld_bytes < 2^31, so the per-lane offsets fit 32 bits and the copies use a scalar
+    // base + vector offset; row r >= i*RPI of copy i keeps every offset non-negative).
     __device__ __forceinline__ void init(const char* row_origin, int64_t ld_bytes, int64_t slab_bytes) {
         const int w = wave_id();
         const int lane = lane_id();
         const int lr = lane / CPR;
         const int pc = lane % CPR;
-        const int r = w * RPI + lr;
-        const int c = SWZ ? (pc ^ swz<CPR>(r)) : pc;
         base = row_origin;
         slab_step = slab_bytes;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            voff[i] = (uint32_t)((int64_t)(r + i * RPI * NW) * ld_bytes + c * 16);
-        lds_wave = w * RPI * ROWB;
+        for (int i = 0; i < IPW; ++i) {
+            const int r = (w * IPW + i) * RPI + lr;
+            const int c = SWZ ? (pc ^ swz<CPR>(r)) : pc;
+            voff[i] = (uint32_t)((int64_t)r * ld_bytes + c * 16 - (i % GROUP) * 1024);
+        }
+        lds_wave = w * IPW * 1024;
+    }
+    // The copies are buffer loads with the LDS bit (a buffer resource based at the slab,
+    // unbounded range, 32-bit lane offsets): unlike the flat-encoded global form they do
+    // not count against the LDS counter, so waits for fragment reads stay exact.
+    template <int IMM>
+    static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t off, LDS_AS char* m0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, m0, 16, off, 0, IMM, 0);
     }
     // Copies [i0, i1) of this wave's IPW copies of slab `slab` (compile-time range
     // after unrolling).
     __device__ __forceinline__ void issue(int slab, LDS_AS char* lds_tile, int i0, int i1) const {
         const char* g = base + (int64_t)slab * slab_step;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, -1, kBufferFlags);
 #pragma unroll
-        for (int i = 0; i < IPW; ++i)
-            if (i >= i0 && i < i1) copy16_to_lds(g + voff[i], lds_tile + lds_wave + i * (RPI * NW * ROWB));
+        for (int i = 0; i < IPW; ++i) {
+            if (i >= i0 && i < i1) {
+                LDS_AS char* m0 = lds_tile + lds_wave + (i / GROUP) * (GROUP * 1024);
+                switch (i % GROUP) {
+                    case 0: copy<0>(rs, voff[i], m0); break;
+                    case 1: copy<1024>(rs, voff[i], m0); break;
+                    case 2: copy<2048>(rs, voff[i], m0); break;
+                    default: copy<3072>(rs, voff[i], m0); break;
+                }
+            }
+        }
     }
 };
 
