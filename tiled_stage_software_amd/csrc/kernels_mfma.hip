@@ -422,6 +422,7 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 3) return launch_ring<T, OUT, 128, 128, 64, 2, 2, 3, false, 16>(p, st);
             break;
         case 13:  // tile 1 with pinned issue order
+            if (S == 1) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 1, false, 32, true>(p, st);
             if (S == 2) return launch_ring<T, OUT, 256, 256, 64, 2, 2, 2, false, 32, true>(p, st);
             break;
         case 14:  // tile 4 (spread) with pinned issue order

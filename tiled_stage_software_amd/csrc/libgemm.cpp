@@ -60,11 +60,15 @@ const Tile kMfmaRing[] = {
     {10, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32 instructions
     {11, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // 16x16x32, spread
     {12, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},    // 16x16x32
-    {13, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 1, pinned issue order
+    {13, 256, 256, 64, 256, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 1, pinned issue order
     {14, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 4, pinned
     {15, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 5, pinned
     {16, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 9, pinned
 };
+// The MFMA ring tile used when none is named for a problem of >= 512 output tiles:
+// 256x256x64, two slots, issue order pinned (the fastest measured on 8192^3 bf16).
+constexpr int kMfmaRingDefault = 13;
+
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
 };
@@ -202,7 +206,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
                 t = find_tile(kValuStaged, many ? 1 : 3);
             }
         } else {
-            const Tile* big = find_tile(kMfmaRing, 1);
+            const Tile* big = find_tile(kMfmaRing, kMfmaRingDefault);
             const Tile* mid = find_tile(kMfmaRing, 3);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
             const Tile* pick = opts.tile ? find_tile(kMfmaRing, opts.tile) : (many ? big : mid);
@@ -217,7 +221,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
         switch (kernel) {
             case GEMM_KERNEL_VALU_RING: t = find_tile(kValuRing, id ? id : 1); break;
             case GEMM_KERNEL_VALU_STAGED: t = find_tile(kValuStaged, id ? id : 1); break;
-            case GEMM_KERNEL_MFMA_RING: t = find_tile(kMfmaRing, id ? id : 1); break;
+            case GEMM_KERNEL_MFMA_RING: t = find_tile(kMfmaRing, id ? id : kMfmaRingDefault); break;
             case GEMM_KERNEL_MFMA_STAGED: t = find_tile(kMfmaStaged, id ? id : 1); break;
         }
         if (!t) return fail(GEMM_ERR_UNSUPPORTED, "tile %d not available for kernel %d", opts.tile, kernel);
