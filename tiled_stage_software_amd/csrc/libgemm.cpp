@@ -39,7 +39,7 @@ constexpr int S1 = 1 << 1, S2 = 1 << 2, S3 = 1 << 3, S4 = 1 << 4;
 
 // Instantiated tiles of each family (must match the launch tables of the kernels).
 const Tile kValuRing[] = {
-    {1, 128, 64, 16, 128, S1 | S2 | S3 | S4, 3, (128 * 16 + 16 * 64) * 4},
+    {1, 128, 64, 16, 128, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},
     {2, 64, 64, 16, 256, S1 | S2 | S3 | S4, 2, (64 * 16 + 16 * 64) * 4},
     {3, 32, 32, 16, 64, S1 | S2 | S3 | S4, 2, (32 * 16 + 16 * 32) * 4},
 };

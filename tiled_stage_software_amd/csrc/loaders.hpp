@@ -118,10 +118,12 @@ struct DirectLoader {
 // below r_lim, column indices below c_lim.
 //
 // Per slab the loader takes one of two paths, chosen uniformly for the workgroup:
-// interior slabs with 16-byte-legal alignment use one vector load per 16 bytes; all
-// other slabs use element loads in which an out-of-range element reads element 0 of the
-// operand and is replaced by +0 (select, no lane-divergent branch), so ragged edges and
-// the K tail contribute exactly zero.
+// interior slabs use one 16-byte load per vector (unaligned when the operand's rows are
+// not 16-byte aligned); edge slabs load whole vectors where they lie inside along the
+// contiguous direction (lines beyond the edge read the last valid line and become +0)
+// and element by element only where a vector straddles the end, an out-of-range
+// element reading element 0 of the operand and being replaced by +0, so ragged edges
+// and the K tail contribute exactly zero.
 template <int LR, int LC, int ES, int NT, bool SWZ, bool TRANS>
 struct StagedLoader {
     static constexpr int VE = 16 / ES;               // elements per 16-byte vector
@@ -140,7 +142,7 @@ struct StagedLoader {
     int64_t ld;          // elements
     int r0, c0;          // tile origin (LDS row 0 / col 0 of slab 0), in the operand's index space
     int r_lim, c_lim;    // valid extents
-    bool vec;            // 16-byte vector loads are legal (alignment)
+    bool vec;            // 16-byte vectors are 16-byte aligned (else unaligned loads)
     bool slab_rows;      // slabs advance along LDS rows (else along LDS cols)
 
     __device__ __forceinline__ void init(const char* X_, int64_t ld_, int r0_, int c0_, int r_lim_, int c_lim_,
@@ -169,32 +171,56 @@ struct StagedLoader {
         }
     }
 
+    // One 16-byte vector at element index idx: a plain vector load when the operand's
+    // rows are 16-byte aligned, else an unaligned one (the target allows unaligned
+    // global accesses; elements are always naturally aligned).
+    __device__ __forceinline__ u32x4 ld_vec(int64_t idx) const {
+        if (vec) return *reinterpret_cast<const u32x4*>(X + idx * ES);
+        u32x4 t;
+        __builtin_memcpy(&t, X + idx * ES, 16);
+        return t;
+    }
+
     __device__ __forceinline__ void load(int slab) {
         const int rs = slab_rows ? r0 + slab * LR : r0;
         const int cs = slab_rows ? c0 : c0 + slab * LC;
-        const bool interior = vec && rs + LR <= r_lim && cs + LC <= c_lim;
+        const bool interior = rs + LR <= r_lim && cs + LC <= c_lim;
         if (interior) {
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 int gr, gc;
                 int64_t idx;
                 coords(j, rs, cs, gr, gc, idx);
-                v[j] = *reinterpret_cast<const u32x4*>(X + idx * ES);
+                v[j] = ld_vec(idx);
             }
         } else {
+            // Edge slab.  A vector whose elements all lie inside along the contiguous
+            // direction is loaded whole, from the last valid line when its own line is
+            // outside (then replaced by zeros); only vectors that straddle the end of
+            // the contiguous direction (the K tail, a ragged N / M edge) go element by
+            // element, reading element 0 for anything outside and selecting +0.
 #pragma unroll
             for (int j = 0; j < CH; ++j) {
                 int gr, gc;
                 int64_t idx;
                 coords(j, rs, cs, gr, gc, idx);
+                const bool whole = TRANS ? gr + VE <= r_lim : gc + VE <= c_lim;
+                const bool line_ok = TRANS ? gc < c_lim : gr < r_lim;
                 u32x4 t = {0u, 0u, 0u, 0u};
+                if (whole) {
+                    const int64_t cidx = TRANS ? (int64_t)(line_ok ? gc : c_lim - 1) * ld + gr
+                                               : (int64_t)(line_ok ? gr : r_lim - 1) * ld + gc;
+                    const u32x4 x = ld_vec(cidx);
+                    if (line_ok) t = x;
+                } else {
 #pragma unroll
-                for (int e = 0; e < VE; ++e) {
-                    const bool ok = TRANS ? (gc < c_lim && gr + e < r_lim) : (gr < r_lim && gc + e < c_lim);
-                    uint32_t x = ld_elem(ok ? idx + e : 0);
-                    x = ok ? x : 0u;
-                    if constexpr (ES == 4) t[e] = x;
-                    else t[e >> 1] |= x << ((e & 1) * 16);
+                    for (int e = 0; e < VE; ++e) {
+                        const bool ok = TRANS ? (gc < c_lim && gr + e < r_lim) : (gr < r_lim && gc + e < c_lim);
+                        uint32_t x = ld_elem(ok ? idx + e : 0);
+                        x = ok ? x : 0u;
+                        if constexpr (ES == 4) t[e] = x;
+                        else t[e >> 1] |= x << ((e & 1) * 16);
+                    }
                 }
                 v[j] = t;
             }
