@@ -447,6 +447,10 @@ static hipError_t staged_dispatch(int tile, int S, const GemmParams& p, hipStrea
             if (S == 1) return launch_staged<T, OUT, 128, 128, 32, 2, 2, 1>(p, st);
             if (S == 2) return launch_staged<T, OUT, 128, 128, 32, 2, 2, 2>(p, st);
             break;
+        case 2:  // 128x128x64, 2x2 waves of 64x64 (half the barriers per FLOP)
+            if (S == 1) return launch_staged<T, OUT, 128, 128, 64, 2, 2, 1>(p, st);
+            if (S == 2) return launch_staged<T, OUT, 128, 128, 64, 2, 2, 2>(p, st);
+            break;
     }
     return hipErrorInvalidValue;
 }

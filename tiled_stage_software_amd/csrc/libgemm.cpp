@@ -71,6 +71,7 @@ constexpr int kMfmaRingDefault = 13;
 
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
+    {2, 128, 128, 64, 256, S1 | S2, 2, (128 + 128) * 64 * 2},
 };
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
