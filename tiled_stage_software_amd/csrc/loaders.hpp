@@ -43,29 +43,36 @@ constexpr int kBufferFlags = 0x00020000;
 // i-th KiB of that band.  The LDS destination of a DMA copy is M0 + the instruction's
 // immediate offset + 16*lane, and the same immediate is added to the global address;
 // so GROUP consecutive copies share one M0 value and step through the band with
-// immediates 0, 1 KiB, ..., the per-lane global offsets having that immediate taken
-// off in advance.  Rewriting M0 between DMA copies stalls the issuing wave, and the
-// wave is the one that feeds the matrix cores.
+// immediates 0, 1 KiB, ...  (rewriting M0 between DMA copies stalls the issuing wave,
+// and that wave is the one that feeds the matrix cores).
+//
+// The global address of lane l in copy i splits into a wave-uniform part -- the copy's
+// first row times the row pitch, less its immediate -- passed as the scalar offset, and a
+// per-lane part that depends only on the lane and on the swizzle phase of the copy's
+// first row (NP phases), so a handful of lane-offset registers serve all copies.
 template <int LR, int ROWB, int NW, bool SWZ>
 struct DirectLoader {
     static constexpr int CPR = ROWB / 16;
     static constexpr int RPI = 64 / CPR;            // LDS rows per copy instruction
     static constexpr int IPW = LR / (RPI * NW);     // copies per wave per slab
     static constexpr int GROUP = 4;                 // copies per M0 value (immediates < 4 KiB)
+    // swizzle phases of a copy's first row (the swizzle has period 16 in the row index)
+    static constexpr int NP = SWZ ? (RPI >= 16 ? 1 : 16 / RPI) : 1;
     static_assert(ROWB % 16 == 0 && CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row bytes");
     static_assert(IPW >= 1 && IPW * RPI * NW == LR, "rows must split evenly over the waves");
     static_assert(RPI * ROWB == 1024, "one copy fills 1 KiB of LDS");
+    static_assert(IPW % NP == 0, "the phase of copy i must not depend on the wave");
 
     const char* base;      // uniform: address of LDS row 0, chunk 0 of slab 0
     int64_t slab_step;     // uniform: bytes between consecutive slabs
-    uint32_t voff[IPW];    // per lane: global byte offset of its chunk in copy i, minus
-                           // the immediate that copy carries
+    uint32_t vpat[NP];     // per lane: row-in-copy * pitch + swizzled chunk, per phase
+    uint32_t soff[IPW];    // uniform: first row of copy i * pitch - copy i's immediate
     int lds_wave;          // uniform: LDS byte offset of this wave's band
 
     // row_origin: global address of LDS row 0 / chunk 0 in slab 0; ld_bytes: bytes
     // between consecutive LDS rows in global memory (ld_bytes >= ROWB, and the host keeps
-    // LR*ld_bytes < 2^31, so the per-lane offsets fit 32 bits and the copies use a scalar
-    // base + vector offset; row r >= i*RPI of copy i keeps every offset non-negative).
+    // LR*ld_bytes < 2^31, so every offset fits 32 bits; copy i starts at row >= i*RPI,
+    // so its scalar offset is never negative).
     __device__ __forceinline__ void init(const char* row_origin, int64_t ld_bytes, int64_t slab_bytes) {
         const int w = wave_id();
         const int lane = lane_id();
@@ -74,19 +81,21 @@ struct DirectLoader {
         base = row_origin;
         slab_step = slab_bytes;
 #pragma unroll
-        for (int i = 0; i < IPW; ++i) {
-            const int r = (w * IPW + i) * RPI + lr;
-            const int c = SWZ ? (pc ^ swz<CPR>(r)) : pc;
-            voff[i] = (uint32_t)((int64_t)r * ld_bytes + c * 16 - (i % GROUP) * 1024);
+        for (int ph = 0; ph < NP; ++ph) {
+            const int c = SWZ ? (pc ^ swz<CPR>(ph * RPI + lr)) : pc;
+            vpat[ph] = (uint32_t)((int64_t)lr * ld_bytes + c * 16);
         }
+#pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            soff[i] = (uint32_t)((int64_t)((w * IPW + i) * RPI) * ld_bytes - (i % GROUP) * 1024);
         lds_wave = w * IPW * 1024;
     }
     // The copies are buffer loads with the LDS bit (a buffer resource based at the slab,
-    // unbounded range, 32-bit lane offsets): unlike the flat-encoded global form they do
-    // not count against the LDS counter, so waits for fragment reads stay exact.
+    // unbounded range): unlike the flat-encoded global form they do not count against the
+    // LDS counter, so waits for fragment reads stay exact.
     template <int IMM>
-    static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t off, LDS_AS char* m0) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, m0, 16, off, 0, IMM, 0);
+    static __device__ __forceinline__ void copy(__amdgpu_buffer_rsrc_t rs, uint32_t voff, uint32_t so, LDS_AS char* m0) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, m0, 16, voff, so, IMM, 0);
     }
     // Copies [i0, i1) of this wave's IPW copies of slab `slab` (compile-time range
     // after unrolling).
@@ -97,11 +106,12 @@ struct DirectLoader {
         for (int i = 0; i < IPW; ++i) {
             if (i >= i0 && i < i1) {
                 LDS_AS char* m0 = lds_tile + lds_wave + (i / GROUP) * (GROUP * 1024);
+                const uint32_t vo = vpat[i % NP];
                 switch (i % GROUP) {
-                    case 0: copy<0>(rs, voff[i], m0); break;
-                    case 1: copy<1024>(rs, voff[i], m0); break;
-                    case 2: copy<2048>(rs, voff[i], m0); break;
-                    default: copy<3072>(rs, voff[i], m0); break;
+                    case 0: copy<0>(rs, vo, soff[i], m0); break;
+                    case 1: copy<1024>(rs, vo, soff[i], m0); break;
+                    case 2: copy<2048>(rs, vo, soff[i], m0); break;
+                    default: copy<3072>(rs, vo, soff[i], m0); break;
                 }
             }
         }
