@@ -102,6 +102,51 @@ class Workload:
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps
 
+    def time_min(self, steps: int, **opts):
+        """Fastest single launch (ms), each launch bracketed by its own events."""
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for a, b in ev:
+            a.record(self.stream)
+            self.step(**opts)
+            b.record(self.stream)
+        torch.cuda.synchronize()
+        return min(a.elapsed_time(b) for a, b in ev)
+
+    def compulsory_bytes(self):
+        """A and B read once, C written once (and read once when beta != 0)."""
+        p = self.p
+        s_in = 4 if p.dtype == "f32" else 2
+        s_out = 4 if p.out == "f32" else 2
+        return (p.M * p.K + p.K * p.N) * s_in + p.M * p.N * s_out * (2 if p.beta != 0 else 1)
+
+
+def pipe_copy_control(dev, mib: int = 1024, reps: int = 20):
+    """The bandwidth-bound control: GB/s (bytes read + written) of the nStage-pipelined
+    streaming copy for each stage count."""
+    n = mib << 20
+    src = torch.empty(n, dtype=torch.uint8, device=dev).random_(0, 256)
+    dst = torch.empty_like(src)
+    st = torch.cuda.current_stream(dev)
+    out = {}
+    for S in (1, 2, 3, 4):
+        for _ in range(3):
+            lg.check(lg.gemm_pipe_copy(dst.data_ptr(), src.data_ptr(), n, S, st.cuda_stream))
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            lg.gemm_pipe_copy(dst.data_ptr(), src.data_ptr(), n, S, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        out[str(S)] = {"ms": round(ms, 4), "GB/s": round(2 * n / (ms * 1e-3) / 1e9, 1)}
+    ok = bool(torch.equal(src, dst))
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"what": f"nStage-pipelined streaming copy of {mib} MiB (same ring protocol), bytes read + written",
+            "nstage": out, "copy_exact": ok, "hbm_peak_GB/s": 8000}
+
 
 def cpu_baseline(w: Workload, target_s: float, nthreads: int):
     """Time the oracle (as it stands) on a bounded row sample of the workload on the host
@@ -221,6 +266,9 @@ def main():
             entry["ms"] = round(t, 5)
             entry["tflops"] = round(ww.flops / (t * 1e-3) / 1e12, 2)
             entry["frac_of_peak"] = round(entry["tflops"] / PEAK[ww.p.dtype], 4)
+            tmin = ww.time_min(min(reps, 30))
+            entry["ms_min"] = round(tmin, 5)
+            entry["compulsory_hbm_GB/s"] = round(ww.compulsory_bytes() / (t * 1e-3) / 1e9, 1)
             # pipelining comparison on the ring kernel of the default tile
             if pl.kernel in (lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING):
                 stages = {}
@@ -239,6 +287,7 @@ def main():
                 del ww
                 torch.cuda.empty_cache()
         rec["workloads"] = sweep
+        rec["negative_control"] = pipe_copy_control(dev)
 
     if not args.no_cpu_baseline:
         w.reset_c()

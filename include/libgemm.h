@@ -163,6 +163,18 @@ gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
  * arguments. */
 int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity);
 
+/* dst[0, bytes) = src[0, bytes), streamed through an nStage LDS ring by the same K-loop
+ * protocol and global->LDS copies as the GEMM kernels (16 KiB slabs, each workgroup a
+ * contiguous run of them; each slab is copied into LDS, then written out).  It is the
+ * bandwidth-bound control of software pipelining: the page "Software Pipelining and
+ * Double Buffering" (section "When it pays") says extra stages change nothing for a
+ * kernel that already saturates memory bandwidth.
+ * dst, src: device pointers, 16-byte aligned, not overlapping; bytes: a multiple of
+ * 16384 (0 = no-op); nstage: 1..4 LDS slots (0 = 2).  Enqueued on `stream`.
+ * Errors: GEMM_ERR_INVALID_ARG (size, alignment, NULL, overlap), GEMM_ERR_UNSUPPORTED
+ * (nstage), GEMM_ERR_HIP (launch). */
+gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nstage, hipStream_t stream);
+
 const char* gemm_status_string(gemm_status_t status);
 
 /* Thread-local description of the last non-OK status on this thread ("" if none). */

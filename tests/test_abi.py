@@ -159,3 +159,22 @@ def test_forced_kernels_and_stages():
         assert s == 0 and p.nstage == S and p.lds_bytes == S * (128 * 16 + 16 * 64) * 4
     s, p = plan(F32, F32, COL, COL, 100, 70, 33, kernel=lg.GEMM_KERNEL_VALU_STAGED, nstage=1)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_STAGED and p.nstage == 1
+
+
+def test_pipe_copy_rejects_bad_arguments_before_launching():
+    """Every error path of gemm_pipe_copy returns before any HIP call (runs without a GPU)."""
+    S = 16384
+    cases = [
+        (A16, B16, -S, 2, lg.GEMM_ERR_INVALID_ARG),          # negative size
+        (A16, B16, S + 16, 2, lg.GEMM_ERR_INVALID_ARG),      # not a multiple of a slab
+        (A16, B16, S, 5, lg.GEMM_ERR_UNSUPPORTED),           # stage count
+        (A16, B16, S, -1, lg.GEMM_ERR_UNSUPPORTED),
+        (0, B16, S, 2, lg.GEMM_ERR_INVALID_ARG),             # NULL
+        (A16, 0, S, 2, lg.GEMM_ERR_INVALID_ARG),
+        (A16 + 4, B16, S, 2, lg.GEMM_ERR_INVALID_ARG),       # alignment
+        (A16, A16 + S // 2, S, 2, lg.GEMM_ERR_INVALID_ARG),  # overlap
+    ]
+    for dst, src, n, st, want in cases:
+        assert lg.gemm_pipe_copy(dst, src, n, st) == want, (dst, src, n, st)
+        assert lg.gemm_last_error()
+    assert lg.gemm_pipe_copy(0, 0, 0, 2) == lg.GEMM_OK       # empty copy: nothing launched

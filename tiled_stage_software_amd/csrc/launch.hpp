@@ -13,4 +13,16 @@ hipError_t launch_mfma_ring(int in_type, int tile, int nstage, const GemmParams&
 hipError_t launch_mfma_staged(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st);
 hipError_t launch_scale(const GemmParams& p, hipStream_t st);
 
+// Pipelined streaming copy (the bandwidth-bound control): `slabs` slabs of kCopySlab
+// bytes, per_wg consecutive slabs per workgroup.
+constexpr int kCopySlab = 16384;
+constexpr int kCopyThreads = 256;
+struct CopyParams {
+    const char* src;
+    char* dst;
+    int64_t slabs;
+    int64_t per_wg;
+};
+hipError_t launch_pipe_copy(int nstage, const CopyParams& p, int64_t grid, hipStream_t st);
+
 }  // namespace gemm

@@ -413,6 +413,31 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
     return n;
 }
 
+gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nstage, hipStream_t stream) {
+    g_err[0] = 0;
+    if (bytes < 0) return fail(GEMM_ERR_INVALID_ARG, "bytes %lld < 0", (long long)bytes);
+    if (nstage < 0 || nstage > 4) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d: the copy ring has 1..4 slots", nstage);
+    if (bytes % gemm::kCopySlab != 0)
+        return fail(GEMM_ERR_INVALID_ARG, "bytes %lld is not a multiple of %d", (long long)bytes, gemm::kCopySlab);
+    if (bytes == 0) return GEMM_OK;
+    if (!dst || !src) return fail(GEMM_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(dst) || !aligned16(src)) return fail(GEMM_ERR_INVALID_ARG, "dst and src must be 16-byte aligned");
+    const char* s0 = static_cast<const char*>(src);
+    const char* d0 = static_cast<const char*>(dst);
+    if (s0 < d0 + bytes && d0 < s0 + bytes) return fail(GEMM_ERR_INVALID_ARG, "dst and src overlap");
+    gemm::CopyParams p;
+    p.src = s0;
+    p.dst = static_cast<char*>(dst);
+    p.slabs = bytes / gemm::kCopySlab;
+    // about 8 workgroups per CU, each streaming a contiguous run of slabs
+    const int64_t max_wg = 2048;
+    p.per_wg = (p.slabs + max_wg - 1) / max_wg;
+    const int64_t grid = (p.slabs + p.per_wg - 1) / p.per_wg;
+    const hipError_t e = gemm::launch_pipe_copy(nstage ? nstage : 2, p, grid, stream);
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GEMM_OK;
+}
+
 const char* gemm_status_string(gemm_status_t s) {
     switch (s) {
         case GEMM_OK: return "GEMM_OK";

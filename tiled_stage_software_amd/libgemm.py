@@ -31,7 +31,7 @@ KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: 
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
-           "gemm_plan", "gemm_schedule", "gemm_status_string", "gemm_last_error")
+           "gemm_plan", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string", "gemm_last_error")
 
 
 class GemmOpts(ctypes.Structure):
@@ -84,6 +84,8 @@ def load():
         lib.gemm_plan.restype = i32
         lib.gemm_schedule.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int), i32]
         lib.gemm_schedule.restype = i32
+        lib.gemm_pipe_copy.argtypes = [vp, vp, i64, i32, vp]
+        lib.gemm_pipe_copy.restype = i32
         lib.gemm_status_string.argtypes = [i32]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_last_error.argtypes = []
@@ -145,6 +147,11 @@ def gemm_schedule(kernel, nstage, num_k, ksteps):
     buf = (ctypes.c_int * (4 * max(n, 1)))()
     lib.gemm_schedule(kernel, nstage, num_k, ksteps, buf, n)
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def gemm_pipe_copy(dst: int, src: int, nbytes: int, nstage: int = 0, stream: int = 0) -> int:
+    """dst[0, nbytes) = src[0, nbytes) through the nStage LDS ring (device pointers)."""
+    return load().gemm_pipe_copy(dst, src, nbytes, nstage, stream)
 
 
 def gemm_status_string(s: int) -> str:
