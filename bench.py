@@ -282,6 +282,14 @@ def main():
                     ts = ww.time(reps, 5, nstage=S, kernel=pl.kernel, tile=pl.tile)
                     stages[str(S)] = {"ms": round(ts, 5), "tflops": round(ww.flops / (ts * 1e-3) / 1e12, 2)}
                 entry["nstage_sweep"] = stages
+            # the stage / tile tuner's pick for this problem (measured, not modelled)
+            ts_, best, bms = lg.gemm_tune(DT_CODE[ww.p.dtype], DT_CODE[ww.p.out], ww.p.A.layout, ww.p.B.layout,
+                                          ww.p.M, ww.p.N, ww.p.K, ww.p.alpha, ww.A.data_ptr(), ww.p.A.ld,
+                                          ww.B.data_ptr(), ww.p.B.ld, ww.p.beta, ww.C.data_ptr(), ww.p.N,
+                                          ww.stream.cuda_stream, reps=200 if name == "c1" else 10)
+            lg.check(ts_)
+            entry["tuned"] = {"kernel": best.kernel, "tile": best.tile, "nstage": best.nstage, "ms": round(bms, 5),
+                              "tflops": round(ww.flops / (bms * 1e-3) / 1e12, 2)}
             sweep[name] = entry
             if ww is not w:
                 del ww

@@ -144,6 +144,26 @@ gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
                         const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
                         const gemm_opts_t* opts, gemm_plan_t* plan);
 
+/* Stage / tile tuner: launch every (kernel family, tile, stage count) that gemm_plan
+ * accepts for this problem -- one warm-up call and `reps` timed calls each, HIP events on
+ * `stream` -- and return the fastest as *best (pass it to gemm_*_ex) with its average
+ * time per call in *best_ms.  The stage count is chosen against the measured curve rather
+ * than a model (the page "Software Pipelining and Double Buffering", section
+ * "Multi-stage pipelines", ties the useful depth to the shared-memory budget; section 7
+ * of "CUTLASS-Cute 初步(6)：CUDA GEMM 计算优化、Multi-Stage 与软流水" models it from
+ * bandwidth and compute rates).
+ * Arguments as gemm_plan plus: C is overwritten by the timed calls (with beta != 0 its
+ * contents afterwards are unspecified: the calls accumulate); reps 1..100000.
+ * Synchronises `stream`.  Empty problems and quick returns report the default plan with
+ * *best_ms = 0.  Different tiles sum in different orders, so results differ in the last
+ * bits between choices (each choice is deterministic).
+ * Errors: as gemm_plan, GEMM_ERR_INVALID_ARG for NULL best / best_ms or reps out of
+ * range, GEMM_ERR_HIP for a failed launch or timing. */
+gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb,
+                        int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                        const void* B, int64_t ldb, float beta, void* C, int64_t ldc, hipStream_t stream,
+                        int reps, gemm_opts_t* best, float* best_ms);
+
 /* The K-loop protocol of a kernel family, as the event list its mainloop executes
  * (host only, for checking the pipeline on the CPU).  Each event is 4 ints
  * {type, slab, slot, arg}:

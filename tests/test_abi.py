@@ -178,3 +178,20 @@ def test_pipe_copy_rejects_bad_arguments_before_launching():
         assert lg.gemm_pipe_copy(dst, src, n, st) == want, (dst, src, n, st)
         assert lg.gemm_last_error()
     assert lg.gemm_pipe_copy(0, 0, 0, 2) == lg.GEMM_OK       # empty copy: nothing launched
+
+
+def test_tune_rejects_bad_arguments_before_launching():
+    import ctypes
+    lib = lg.load()
+    best = lg.GemmOpts()
+    ms = ctypes.c_float()
+    args = (BF16, BF16, ROW, COL, 256, 256, 256, 1.0, A16, 256, B16, 256, 0.0, C16, 256, None)
+    assert lib.gemm_tune(*args, 0, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_tune(*args, 5, None, ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
+    assert lib.gemm_tune(*args, 5, ctypes.byref(best), None) == lg.GEMM_ERR_INVALID_ARG
+    bad_type = (7,) + args[1:]
+    assert lib.gemm_tune(*bad_type, 5, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
+    bad_c = (BF16, F16) + args[2:]
+    assert lib.gemm_tune(*bad_c, 5, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
+    bad_ld = args[:9] + (100,) + args[10:]     # lda < K
+    assert lib.gemm_tune(*bad_ld, 5, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG

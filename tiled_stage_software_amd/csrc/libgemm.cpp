@@ -383,6 +383,80 @@ gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
     return choose(q, opts, plan, &gp);
 }
 
+gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
+                        int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float beta, void* C, int64_t ldc, hipStream_t stream, int reps, gemm_opts_t* best,
+                        float* best_ms) {
+    g_err[0] = 0;
+    if (!best || !best_ms) return fail(GEMM_ERR_INVALID_ARG, "best / best_ms is NULL");
+    if (reps < 1 || reps > 100000) return fail(GEMM_ERR_INVALID_ARG, "reps %d", reps);
+    if (in_type != GEMM_F32 && in_type != GEMM_BF16 && in_type != GEMM_F16)
+        return fail(GEMM_ERR_INVALID_ARG, "in_type %d", (int)in_type);
+    if (in_type == GEMM_F32 ? c_type != GEMM_F32 : (c_type != GEMM_F32 && c_type != in_type))
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered for in_type %d", (int)c_type, (int)in_type);
+    Problem q{(int)in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+
+    // the candidates: every (family, tile, stage count) the planner accepts for q
+    struct Cand { int kernel, tile, nstage; };
+    std::vector<Cand> cands;
+    const bool mfma = in_type != GEMM_F32;
+    const int fams[2] = {mfma ? GEMM_KERNEL_MFMA_RING : GEMM_KERNEL_VALU_RING,
+                         mfma ? GEMM_KERNEL_MFMA_STAGED : GEMM_KERNEL_VALU_STAGED};
+    for (int fam : fams) {
+        const Tile* tab = nullptr;
+        size_t n = 0;
+        if (fam == GEMM_KERNEL_VALU_RING) { tab = kValuRing; n = sizeof(kValuRing) / sizeof(Tile); }
+        if (fam == GEMM_KERNEL_VALU_STAGED) { tab = kValuStaged; n = sizeof(kValuStaged) / sizeof(Tile); }
+        if (fam == GEMM_KERNEL_MFMA_RING) { tab = kMfmaRing; n = sizeof(kMfmaRing) / sizeof(Tile); }
+        if (fam == GEMM_KERNEL_MFMA_STAGED) { tab = kMfmaStaged; n = sizeof(kMfmaStaged) / sizeof(Tile); }
+        for (size_t t = 0; t < n; ++t)
+            for (int S = 1; S <= GEMM_MAX_NSTAGE; ++S) {
+                gemm_opts_t o = {S, fam, tab[t].id, 0};
+                gemm_plan_t pl;
+                GemmParams gp;
+                if (choose(q, &o, &pl, &gp) == GEMM_OK && pl.grid > 0) cands.push_back({fam, tab[t].id, S});
+            }
+    }
+    g_err[0] = 0;
+    if (cands.empty()) {
+        // nothing to tune (empty problem or a quick return): report the default choice
+        gemm_plan_t pl;
+        GemmParams gp;
+        s = choose(q, nullptr, &pl, &gp);
+        if (s != GEMM_OK) return s;
+        *best = {pl.nstage, pl.kernel, pl.tile, 0};
+        *best_ms = 0.0f;
+        return GEMM_OK;
+    }
+    hipEvent_t e0, e1;
+    if (hipEventCreate(&e0) != hipSuccess) return fail(GEMM_ERR_HIP, "hipEventCreate failed");
+    if (hipEventCreate(&e1) != hipSuccess) { (void)hipEventDestroy(e0); return fail(GEMM_ERR_HIP, "hipEventCreate failed"); }
+    float best_t = -1.0f;
+    gemm_status_t result = GEMM_OK;
+    for (const Cand& c : cands) {
+        gemm_opts_t o = {c.nstage, c.kernel, c.tile, 0};
+        s = run(q, &o, stream);                      // warm-up (code load, caches)
+        if (s != GEMM_OK) { result = s; break; }
+        hipError_t he = hipEventRecord(e0, stream);
+        for (int r = 0; r < reps && s == GEMM_OK; ++r) s = run(q, &o, stream);
+        if (s != GEMM_OK) { result = s; break; }
+        if (he == hipSuccess) he = hipEventRecord(e1, stream);
+        if (he == hipSuccess) he = hipEventSynchronize(e1);
+        float ms = 0.0f;
+        if (he == hipSuccess) he = hipEventElapsedTime(&ms, e0, e1);
+        if (he != hipSuccess) { result = fail(GEMM_ERR_HIP, "timing failed: %s", hipGetErrorString(he)); break; }
+        ms /= (float)reps;
+        if (best_t < 0.0f || ms < best_t) { best_t = ms; *best = o; }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (result != GEMM_OK) return result;
+    *best_ms = best_t;
+    return GEMM_OK;
+}
+
 int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity) {
     if (num_k < 0 || capacity < 0 || (capacity > 0 && !events)) return -1;
     Recorder r;

@@ -31,7 +31,8 @@ KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: 
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
-           "gemm_plan", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string", "gemm_last_error")
+           "gemm_plan", "gemm_tune", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string",
+           "gemm_last_error")
 
 
 class GemmOpts(ctypes.Structure):
@@ -84,6 +85,9 @@ def load():
         lib.gemm_plan.restype = i32
         lib.gemm_schedule.argtypes = [i32, i32, i32, i32, ctypes.POINTER(ctypes.c_int), i32]
         lib.gemm_schedule.restype = i32
+        lib.gemm_tune.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                                  vp, i32, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_float)]
+        lib.gemm_tune.restype = i32
         lib.gemm_pipe_copy.argtypes = [vp, vp, i64, i32, vp]
         lib.gemm_pipe_copy.restype = i32
         lib.gemm_status_string.argtypes = [i32]
@@ -147,6 +151,15 @@ def gemm_schedule(kernel, nstage, num_k, ksteps):
     buf = (ctypes.c_int * (4 * max(n, 1)))()
     lib.gemm_schedule(kernel, nstage, num_k, ksteps, buf, n)
     return [tuple(buf[4 * i:4 * i + 4]) for i in range(n)]
+
+
+def gemm_tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0, reps=10):
+    """(status, GemmOpts of the fastest variant, its ms per call) -- see include/libgemm.h."""
+    best = GemmOpts()
+    ms = ctypes.c_float(0.0)
+    s = load().gemm_tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, reps,
+                         ctypes.byref(best), ctypes.byref(ms))
+    return s, best, ms.value
 
 
 def gemm_pipe_copy(dst: int, src: int, nbytes: int, nstage: int = 0, stream: int = 0) -> int:
