@@ -304,6 +304,85 @@ void mfma_ring_kernel(const GemmParams p) {
     ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
 }
 
+// ---------------------------------------------------------------- wave-specialised ring
+// Producer / consumer split of the same ring: NP producer waves issue every global->LDS
+// copy and wait for it; 4 consumer waves (2x2, wave tile (BM/2) x (BN/2)) only read
+// fragments and run MFMAs, so a copy never blocks the wave that feeds a matrix core.
+// Both roles run the same K-loop template (schedule.hpp) with their half of the work
+// and no-ops for the other half, so they meet at exactly the same barriers: a slab is
+// published by the barrier after the producers' wait, and a slot is overwritten only
+// after the barrier that follows the consumers' last reads of it.
+template <typename T, int BM, int BN, int BK, int S, int NP>
+struct WsProducerOps {
+    static constexpr int ROWB = BK * 2;
+    static constexpr int A_BYTES = BM * ROWB;
+    static constexpr int STAGE = (BM + BN) * ROWB;
+    static constexpr int KS = BK / 16;
+    DirectLoader<BM, ROWB, NP, true> la;
+    DirectLoader<BN, ROWB, NP, true> lb;
+    static constexpr int L = DirectLoader<BM, ROWB, NP, true>::IPW + DirectLoader<BN, ROWB, NP, true>::IPW;
+    LDS_AS char* smem;
+    __device__ __forceinline__ void issue(int slab, int slot, int, int) {
+        LDS_AS char* st = smem + slot * STAGE;
+        la.issue(slab, st, 0, decltype(la)::IPW);
+        lb.issue(slab, st + A_BYTES, 0, decltype(lb)::IPW);
+    }
+    template <int N>
+    __device__ __forceinline__ void wait_slabs() { wait_vm<N * L>(); }
+    __device__ __forceinline__ void wait_lds() {}
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int, int) {}
+    template <int BUF, int HAS, int PARTS>
+    __device__ __forceinline__ void math(int) {}
+};
+
+template <typename T, int BM, int BN, int BK>
+struct WsConsumerOps : MfmaCompute<T, BM, BN, BK, 2, 2, 32> {
+    typedef MfmaCompute<T, BM, BN, BK, 2, 2, 32> C;
+    __device__ __forceinline__ void issue(int, int, int, int) {}
+    template <int N>
+    __device__ __forceinline__ void wait_slabs() {}
+    __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    template <int BUF, int HAS, int PARTS>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, 0>(); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int S, int NP>
+__global__ __launch_bounds__((4 + NP) * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_ws_kernel(const GemmParams p) {
+    static constexpr int STAGE = (BM + BN) * BK * 2;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m_keep = tm * BM, n_keep = tn * BN;
+    const int m0 = min(m_keep, p.M - BM);
+    const int n0 = min(n_keep, p.N - BN);
+    const int numK = p.K / BK;
+    if (wave_id() >= 4) {
+        WsProducerOps<T, BM, BN, BK, S, NP> ops;
+        ops.smem = (LDS_AS char*)(smem_raw);
+        ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2, wave_id() - 4);
+        ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2, wave_id() - 4);
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, numK);
+    } else {
+        WsConsumerOps<T, BM, BN, BK> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, numK);
+        ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+    }
+}
+
+template <typename T, int OUT, int BM, int BN, int BK, int S, int NP>
+static hipError_t launch_ws(const GemmParams& p, hipStream_t st) {
+    const int grid = p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((mfma_ws_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), 0, st, p);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- staged kernel
 // AT / BT: the operand is contiguous across the LDS rows (A column-major, B row-major)
 // and is transposed on its way into the K-contiguous LDS tile.
@@ -431,6 +510,14 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
         case 15:  // tile 5 (256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 3, true, 32, true>(p, st);
             if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 4, true, 32, true>(p, st);
+            break;
+        case 17:  // 256x128x64, 4 consumer waves (128x64) + 4 producer waves
+            if (S == 2) return launch_ws<T, OUT, 256, 128, 64, 2, 4>(p, st);
+            if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 4>(p, st);
+            break;
+        case 18:  // 256x128x64, 4 consumer waves + 2 producer waves
+            if (S == 2) return launch_ws<T, OUT, 256, 128, 64, 2, 2>(p, st);
+            if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 2>(p, st);
             break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);

@@ -64,6 +64,8 @@ const Tile kMfmaRing[] = {
     {14, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 4, pinned
     {15, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 5, pinned
     {16, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 9, pinned
+    {17, 256, 128, 64, 512, S2 | S3, 2, (256 + 128) * 64 * 2},    // 4 consumer + 4 producer waves
+    {18, 256, 128, 64, 384, S2 | S3, 2, (256 + 128) * 64 * 2},    // 4 consumer + 2 producer waves
 };
 // The MFMA ring tile used when none is named for a problem of >= 512 output tiles:
 // 256x256x64, two slots, issue order pinned (the fastest measured on 8192^3 bf16).

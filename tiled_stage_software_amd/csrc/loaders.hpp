@@ -73,8 +73,9 @@ struct DirectLoader {
     // between consecutive LDS rows in global memory (ld_bytes >= ROWB, and the host keeps
     // LR*ld_bytes < 2^31, so every offset fits 32 bits; copy i starts at row >= i*RPI,
     // so its scalar offset is never negative).
-    __device__ __forceinline__ void init(const char* row_origin, int64_t ld_bytes, int64_t slab_bytes) {
-        const int w = wave_id();
+    // w: index of this wave among the NW loading waves (default: its index in the workgroup).
+    __device__ __forceinline__ void init(const char* row_origin, int64_t ld_bytes, int64_t slab_bytes, int w = -1) {
+        if (w < 0) w = wave_id();
         const int lane = lane_id();
         const int lr = lane / CPR;
         const int pc = lane % CPR;
