@@ -103,7 +103,9 @@ typedef struct gemm_plan {
     int bm, bn, bk;    /* block tile (C rows, C cols, K-slab depth) */
     int threads;       /* threads per workgroup */
     int lds_bytes;     /* LDS per workgroup */
-    int64_t grid;      /* workgroups launched (0 if nothing is launched) */
+    int64_t grid;      /* workgroups launched (0 if nothing is launched); for the persistent
+                          MFMA ring tiles (19, 20) the number of output tiles, which one
+                          workgroup per compute unit walks */
 } gemm_plan_t;
 
 /* fp32 A, B, C. */

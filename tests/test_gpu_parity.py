@@ -200,6 +200,9 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, [1, 2, 3, 4], 512, 768, 640),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 3, [1, 2, 3, 4], 384, 256, 704),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, [3, 4], 512, 768, 640),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 13, [1, 2], 768, 512, 512),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
+    ("f16", "f16", ROW, COL, K_MFMA_RING, 19, [2, 3], 2304, 4352, 320),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
 ]
@@ -377,3 +380,25 @@ def test_every_planned_variant_launches_and_matches(v):
     p = problem(dt, dt if dt != "f32" else "f32", 512, 512, 384, la, lb, dist="int2", seed=61)
     got = run(p, kernel=kern, tile=tile, nstage=S)
     assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
+
+
+# --------------------------------------------------------------- persistent tiles
+
+PERSISTENT = [(19, 2), (19, 3), (20, 3)]
+
+
+@pytest.mark.parametrize("shape", [(4096, 4096, 192), (4100, 3000, 320), (2048, 2560, 128)],
+                         ids=lambda s: "x".join(map(str, s)))
+@pytest.mark.parametrize("ts", PERSISTENT, ids=lambda t: f"t{t[0]}-s{t[1]}")
+def test_persistent_tiles_walk_several_tiles_exactly(shape, ts):
+    """One workgroup per CU walks more tiles than the grid holds (512 and 408 tiles of
+    256x128; 160 fits at once); ragged M / N edges; every element exact on small integers,
+    and the same bits as the non-persistent producer / consumer tile."""
+    M, N, K = shape
+    tile, S = ts
+    say(f"[persistent] tile={tile} S={S} {M}x{N}x{K}")
+    p = problem("bf16", "f32", M, N, K, ROW, COL, dist="int2", seed=83)
+    got = run(p, kernel=K_MFMA_RING, tile=tile, nstage=S)
+    assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
+    ref = run(p, kernel=K_MFMA_RING, tile=18, nstage=S)
+    assert torch.equal(got, ref)

@@ -87,8 +87,10 @@ __host__ __device__ __forceinline__ constexpr int swz(int r) {
 // Workgroup id -> (tile_m, tile_n).  Workgroups are dispatched round-robin over the 8
 // XCDs, each with its own L2; the remap gives each XCD a contiguous run of the grouped
 // order so that the tiles resident on one XCD share A row-panels and B column-panels.
-__device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
-    int wg = blockIdx.x;
+// wg: the workgroup index (a persistent workgroup passes the index of the tile slot it
+// is working on: its own id plus a multiple of the grid size, a multiple of 8, so the
+// slot stays on the workgroup's XCD).
+__device__ __forceinline__ void tile_coords_of(const GemmParams& p, int wg, int& tm, int& tn) {
     const int total = p.tiles_m * p.tiles_n;
     if (p.xcd_remap && (total & 7) == 0) wg = (wg & 7) * (total >> 3) + (wg >> 3);
     const int per_group = p.group_m * p.tiles_n;
@@ -98,6 +100,9 @@ __device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& t
     const int r = wg - g * per_group;
     tm = first_m + r % gsize;
     tn = r / gsize;
+}
+__device__ __forceinline__ void tile_coords(const GemmParams& p, int& tm, int& tn) {
+    tile_coords_of(p, blockIdx.x, tm, tn);
 }
 
 // ---------------------------------------------------------------- epilogue helpers

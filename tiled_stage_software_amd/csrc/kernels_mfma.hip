@@ -383,6 +383,87 @@ static hipError_t launch_ws(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
+// Persistent form: one workgroup per CU walks tile slots wg, wg + G, wg + 2G, ... (G =
+// grid size) and runs ONE ring over the concatenation of their K-slabs (slab g = tile
+// g / numK, K-slab g mod numK).  The producers stream the next tile's first slabs while
+// the consumers finish the current tile and store it, so no tile pays the ring's fill.
+template <typename T, int BM, int BN, int BK, int S, int NP>
+struct WspProducerOps : WsProducerOps<T, BM, BN, BK, S, NP> {
+    typedef WsProducerOps<T, BM, BN, BK, S, NP> P;
+    const GemmParams* gp;
+    int numK, wg, G;
+    __device__ __forceinline__ void issue(int g, int slot, int, int) {
+        const int j = g / numK, kt = g - j * numK;
+        int tm, tn;
+        tile_coords_of(*gp, wg + j * G, tm, tn);
+        const int m0 = min(tm * BM, gp->M - BM), n0 = min(tn * BN, gp->N - BN);
+        LDS_AS char* st = this->smem + slot * P::STAGE;
+        this->la.issue_at(gp->A + ((int64_t)m0 * gp->lda + (int64_t)kt * BK) * 2, st, 0, decltype(this->la)::IPW);
+        this->lb.issue_at(gp->B + ((int64_t)n0 * gp->ldb + (int64_t)kt * BK) * 2, st + P::A_BYTES, 0,
+                          decltype(this->lb)::IPW);
+    }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK>
+struct WspConsumerOps : WsConsumerOps<T, BM, BN, BK> {
+    typedef MfmaCompute<T, BM, BN, BK, 2, 2, 32> C;
+    const GemmParams* gp;
+    int numK, wg, G;
+    // after the last k-step of slab g: if g ends a tile, store the tile and start the next
+    __device__ __forceinline__ void after_slab(int g) {
+        const int j = g / numK;
+        if (g - j * numK != numK - 1) return;
+        int tm, tn;
+        tile_coords_of(*gp, wg + j * G, tm, tn);
+        const int m_keep = tm * BM, n_keep = tn * BN;
+        this->template epilogue<OUT>(*gp, min(m_keep, gp->M - BM), min(n_keep, gp->N - BN), m_keep, n_keep);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int q = 0; q < C::TN; ++q)
+#pragma unroll
+                for (int e = 0; e < C::NR; ++e) this->acc[i][q][e] = 0.0f;
+    }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int S, int NP>
+__global__ __launch_bounds__((4 + NP) * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_wsp_kernel(const GemmParams p) {
+    static constexpr int STAGE = (BM + BN) * BK * 2;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int total = p.tiles_m * p.tiles_n;
+    const int ntiles = wg < total ? (total - wg + G - 1) / G : 0;
+    const int numK = p.K / BK;
+    const int nslabs = ntiles * numK;
+    if (wave_id() >= 4) {
+        WspProducerOps<T, BM, BN, BK, S, NP> ops;
+        ops.smem = (LDS_AS char*)(smem_raw);
+        ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
+        ops.la.init(p.A, p.lda * 2, BK * 2, wave_id() - 4);
+        ops.lb.init(p.B, p.ldb * 2, BK * 2, wave_id() - 4);
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+    } else {
+        WspConsumerOps<T, OUT, BM, BN, BK> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+    }
+}
+
+template <typename T, int OUT, int BM, int BN, int BK, int S, int NP>
+static hipError_t launch_wsp(const GemmParams& p, hipStream_t st) {
+    const int total = p.tiles_m * p.tiles_n;
+    // one workgroup per CU (the ring takes most of the LDS); a multiple of 8 keeps each
+    // tile slot on its workgroup's XCD
+    int grid = num_compute_units();
+    grid -= grid & 7;
+    if (grid < 8) grid = 8;
+    if (grid > total) grid = total;
+    hipLaunchKernelGGL((mfma_wsp_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), 0, st, p);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- staged kernel
 // AT / BT: the operand is contiguous across the LDS rows (A column-major, B row-major)
 // and is transposed on its way into the K-contiguous LDS tile.
@@ -512,12 +593,21 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 2, 4, true, 32, true>(p, st);
             break;
         case 17:  // 256x128x64, 4 consumer waves (128x64) + 4 producer waves
+            if (S == 1) return launch_ws<T, OUT, 256, 128, 64, 1, 4>(p, st);
             if (S == 2) return launch_ws<T, OUT, 256, 128, 64, 2, 4>(p, st);
             if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 4>(p, st);
             break;
         case 18:  // 256x128x64, 4 consumer waves + 2 producer waves
+            if (S == 1) return launch_ws<T, OUT, 256, 128, 64, 1, 2>(p, st);
             if (S == 2) return launch_ws<T, OUT, 256, 128, 64, 2, 2>(p, st);
             if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 2>(p, st);
+            break;
+        case 19:  // tile 18 (4 consumer + 2 producer waves), persistent
+            if (S == 2) return launch_wsp<T, OUT, 256, 128, 64, 2, 2>(p, st);
+            if (S == 3) return launch_wsp<T, OUT, 256, 128, 64, 3, 2>(p, st);
+            break;
+        case 20:  // tile 17 (4 consumer + 4 producer waves), persistent
+            if (S == 3) return launch_wsp<T, OUT, 256, 128, 64, 3, 4>(p, st);
             break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);

@@ -13,6 +13,9 @@ hipError_t launch_mfma_ring(int in_type, int tile, int nstage, const GemmParams&
 hipError_t launch_mfma_staged(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st);
 hipError_t launch_scale(const GemmParams& p, hipStream_t st);
 
+// Compute units of the current device (cached per device; 256 if the query fails).
+int num_compute_units();
+
 // Pipelined streaming copy (the bandwidth-bound control): `slabs` slabs of kCopySlab
 // bytes, per_wg consecutive slabs per workgroup.
 constexpr int kCopySlab = 16384;

@@ -64,12 +64,15 @@ const Tile kMfmaRing[] = {
     {14, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},         // tile 4, pinned
     {15, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 5, pinned
     {16, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 9, pinned
-    {17, 256, 128, 64, 512, S2 | S3, 2, (256 + 128) * 64 * 2},    // 4 consumer + 4 producer waves
-    {18, 256, 128, 64, 384, S2 | S3, 2, (256 + 128) * 64 * 2},    // 4 consumer + 2 producer waves
+    {17, 256, 128, 64, 512, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 4 producer waves
+    {18, 256, 128, 64, 384, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 2 producer waves
+    {19, 256, 128, 64, 384, S2 | S3, 3, (256 + 128) * 64 * 2},    // tile 18, persistent
+    {20, 256, 128, 64, 512, S3, 3, (256 + 128) * 64 * 2},         // tile 17, persistent
 };
-// The MFMA ring tile used when none is named for a problem of >= 512 output tiles:
-// 256x256x64, two slots, issue order pinned (the fastest measured on 8192^3 bf16).
-constexpr int kMfmaRingDefault = 13;
+// The MFMA ring tile used when none is named for a problem of >= 512 256x256 tiles:
+// 256x128x64, three slots, 2 producer waves feeding 4 consumer waves (the fastest
+// measured on 8192^3 bf16; on par with the 256x256 tiles on the f16 MLP shape).
+constexpr int kMfmaRingDefault = 18;
 
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},

@@ -101,7 +101,11 @@ struct DirectLoader {
     // Copies [i0, i1) of this wave's IPW copies of slab `slab` (compile-time range
     // after unrolling).
     __device__ __forceinline__ void issue(int slab, LDS_AS char* lds_tile, int i0, int i1) const {
-        const char* g = base + (int64_t)slab * slab_step;
+        issue_at(base + (int64_t)slab * slab_step, lds_tile, i0, i1);
+    }
+    // Same, for the slab whose LDS row 0 / chunk 0 is at global address g (another tile's
+    // slab in a persistent kernel; same row pitch).
+    __device__ __forceinline__ void issue_at(const char* g, LDS_AS char* lds_tile, int i0, int i1) const {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, -1, kBufferFlags);
 #pragma unroll
         for (int i = 0; i < IPW; ++i) {

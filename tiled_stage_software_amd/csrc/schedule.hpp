@@ -116,6 +116,13 @@ GEMM_HD void single_slab_compute(Ops& ops, int kt) {
 }
 
 // Direct global->LDS ring.  KS = k-steps per slab (even); SPREAD: see ring_slab.
+// Hook after slab kt's last k-step (a persistent kernel stores a finished tile there);
+// Ops without an after_slab member do nothing.
+template <class O>
+GEMM_HD auto after_slab_(O& o, int kt, int) -> decltype(o.after_slab(kt), void()) { o.after_slab(kt); }
+template <class O>
+GEMM_HD void after_slab_(O&, int, long) {}
+
 template <int S, int KS, bool SPREAD, class Ops>
 GEMM_HD void ring_mainloop(Ops& ops, int numK) {
     static_assert(KS % 2 == 0, "fragment double-buffering needs an even number of k-steps");
@@ -129,6 +136,7 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
             single_slab_compute<KS>(ops, kt);
             ops.wait_lds();
             ops.barrier();
+            after_slab_(ops, kt, 0);
         }
     } else {
         // prologue: slabs 0 .. S-2 (fewer if K is short); wait for slab 0
@@ -147,21 +155,25 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
         for (; kt < main_end - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
             ring_slab<S, KS, SPREAD, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
+            after_slab_(ops, kt, 0);
             slot = next_slot;
             issue_slot = (issue_slot + 1 == S) ? 0 : issue_slot + 1;
         }
         if (kt < main_end) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
             ring_slab<S, KS, SPREAD, BODY_MAIN_END>(ops, kt, slot, issue_slot, next_slot);
+            after_slab_(ops, kt, 0);
             slot = next_slot;
             ++kt;
         }
         for (; kt < numK - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
             ring_slab<S, KS, SPREAD, BODY_TAIL>(ops, kt, slot, 0, next_slot);
+            after_slab_(ops, kt, 0);
             slot = next_slot;
         }
         ring_slab<S, KS, SPREAD, BODY_LAST>(ops, kt, slot, 0, 0);
+        after_slab_(ops, kt, 0);
     }
 }
 
@@ -203,6 +215,7 @@ GEMM_HD void staged_mainloop(Ops& ops, int numK) {
             single_slab_compute<KS>(ops, kt);
             ops.wait_lds();
             ops.barrier();
+            after_slab_(ops, kt, 0);
         }
     } else {
         ops.load(0);
