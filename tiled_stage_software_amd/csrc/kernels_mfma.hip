@@ -609,6 +609,9 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
         case 20:  // tile 17 (4 consumer + 4 producer waves), persistent
             if (S == 3) return launch_wsp<T, OUT, 256, 128, 64, 3, 4>(p, st);
             break;
+        case 22:  // 256x128x64, 4 consumer waves + 1 producer wave
+            if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 1>(p, st);
+            break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);
             if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4, true, 32, true>(p, st);

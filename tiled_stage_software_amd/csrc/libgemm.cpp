@@ -68,6 +68,7 @@ const Tile kMfmaRing[] = {
     {18, 256, 128, 64, 384, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 2 producer waves
     {19, 256, 128, 64, 384, S2 | S3, 3, (256 + 128) * 64 * 2},    // tile 18, persistent
     {20, 256, 128, 64, 512, S3, 3, (256 + 128) * 64 * 2},         // tile 17, persistent
+    {22, 256, 128, 64, 320, S3, 3, (256 + 128) * 64 * 2},         // 4 consumer + 1 producer wave
 };
 // The MFMA ring tile used when none is named for a problem of >= 512 256x256 tiles:
 // 256x128x64, three slots, 2 producer waves feeding 4 consumer waves (the fastest
