@@ -74,11 +74,11 @@ class Workload:
         lg.check(s)
         return pl
 
-    def step(self, nstage=0, kernel=0, tile=0):
+    def step(self, nstage=0, kernel=0, tile=0, flags=0):
         p = self.p
         s = lg.gemm_operands(p.dtype, p.out, p.A.layout, p.B.layout, p.M, p.N, p.K, p.alpha,
                              self.A.data_ptr(), p.A.ld, self.B.data_ptr(), p.B.ld, p.beta, self.C.data_ptr(), p.N,
-                             self.stream.cuda_stream, nstage=nstage, kernel=kernel, tile=tile)
+                             self.stream.cuda_stream, nstage=nstage, kernel=kernel, tile=tile, flags=flags)
         if s != lg.GEMM_OK:
             raise lg.GemmError(s, lg.gemm_last_error())
 
@@ -281,6 +281,10 @@ def main():
                         continue
                     ts = ww.time(reps, 5, nstage=S, kernel=pl.kernel, tile=pl.tile)
                     stages[str(S)] = {"ms": round(ts, 5), "tflops": round(ww.flops / (ts * 1e-3) / 1e12, 2)}
+                    # the same with every stage count given the LDS of the deepest ring
+                    te = ww.time(reps, 5, nstage=S, kernel=pl.kernel, tile=pl.tile, flags=lg.GEMM_FLAG_EQUAL_LDS)
+                    stages[str(S)]["equal_lds_ms"] = round(te, 5)
+                    stages[str(S)]["equal_lds_tflops"] = round(ww.flops / (te * 1e-3) / 1e12, 2)
                 entry["nstage_sweep"] = stages
             # the stage / tile tuner's pick for this problem (measured, not modelled)
             ts_, best, bms = lg.gemm_tune(DT_CODE[ww.p.dtype], DT_CODE[ww.p.out], ww.p.A.layout, ww.p.B.layout,

@@ -94,6 +94,10 @@ typedef struct gemm_opts {
 } gemm_opts_t;
 
 #define GEMM_FLAG_NO_XCD_REMAP 1
+/* Allocate, whatever the stage count, the LDS of the deepest ring the tile offers, so that
+ * nStage variants run at the same occupancy (the fair comparison: at natural occupancy a
+ * shallower ring leaves room for more resident workgroups).  Results are unchanged. */
+#define GEMM_FLAG_EQUAL_LDS 2
 
 /* What a call would launch (filled by gemm_plan; no GPU needed). */
 typedef struct gemm_plan {

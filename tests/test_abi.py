@@ -195,3 +195,21 @@ def test_tune_rejects_bad_arguments_before_launching():
     assert lib.gemm_tune(*bad_c, 5, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
     bad_ld = args[:9] + (100,) + args[10:]     # lda < K
     assert lib.gemm_tune(*bad_ld, 5, ctypes.byref(best), ctypes.byref(ms)) == lg.GEMM_ERR_INVALID_ARG
+
+
+def test_equal_lds_flag_pads_to_the_deepest_ring():
+    """GEMM_FLAG_EQUAL_LDS gives every stage count the LDS of the tile's deepest ring."""
+    deepest = None
+    for S in (1, 2, 3, 4):
+        s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, kernel=lg.GEMM_KERNEL_VALU_RING, tile=1,
+                    flags=lg.GEMM_FLAG_EQUAL_LDS)
+        assert s == 0
+        deepest = deepest or p.lds_bytes
+        assert p.lds_bytes == deepest == 4 * (128 * 16 + 16 * 64) * 4
+        s, q = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, kernel=lg.GEMM_KERNEL_VALU_RING, tile=1)
+        assert q.lds_bytes == S * (128 * 16 + 16 * 64) * 4
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, nstage=1, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=18,
+                flags=lg.GEMM_FLAG_EQUAL_LDS)
+    assert s == 0 and p.lds_bytes == 3 * (256 + 128) * 64 * 2 <= 163840
+    s, _ = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, flags=8)
+    assert s == lg.GEMM_ERR_INVALID_ARG

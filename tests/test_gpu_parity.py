@@ -402,3 +402,20 @@ def test_persistent_tiles_walk_several_tiles_exactly(shape, ts):
     assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
     ref = run(p, kernel=K_MFMA_RING, tile=18, nstage=S)
     assert torch.equal(got, ref)
+
+
+EQUAL_LDS = [("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3], 512, 384, 256),
+             ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2], 768, 640, 576),
+             ("bf16", "bf16", ROW, COL, K_MFMA_RING, 3, [1, 2, 3], 384, 256, 320)]
+
+
+@pytest.mark.parametrize("case", EQUAL_LDS, ids=lambda c: f"{c[0]}-k{c[4]}-t{c[5]}")
+def test_equal_lds_padding_changes_no_bit(case):
+    """The equal-occupancy launches (extra dynamic LDS) give the same bits."""
+    dtype, out, la, lb, kern, tile, stages, M, N, K = case
+    p = problem(dtype, out, M, N, K, la, lb, dist="normal", seed=29)
+    for S in stages:
+        say(f"[equal-lds] {case[:6]} nstage={S}")
+        a = run(p, kernel=kern, tile=tile, nstage=S)
+        b = run(p, kernel=kern, tile=tile, nstage=S, flags=lg.GEMM_FLAG_EQUAL_LDS)
+        assert torch.equal(a, b)

@@ -34,6 +34,7 @@ struct GemmParams {
     int group_m;            // tile rows per rasterisation group
     int xcd_remap;          // 1 = spread consecutive tiles onto one XCD
     int a_vec, b_vec;       // staged kernels: 16-byte vector loads are legal for A / B
+    int lds_pad;            // host only: extra dynamic LDS bytes per workgroup (equal-occupancy runs)
 };
 
 // ---------------------------------------------------------------- waits and barriers

@@ -379,7 +379,7 @@ void mfma_ws_kernel(const GemmParams p) {
 template <typename T, int OUT, int BM, int BN, int BK, int S, int NP>
 static hipError_t launch_ws(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ws_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ws_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), p.lds_pad, st, p);
     return hipGetLastError();
 }
 
@@ -460,7 +460,7 @@ static hipError_t launch_wsp(const GemmParams& p, hipStream_t st) {
     grid -= grid & 7;
     if (grid < 8) grid = 8;
     if (grid > total) grid = total;
-    hipLaunchKernelGGL((mfma_wsp_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_wsp_kernel<T, OUT, BM, BN, BK, S, NP>), dim3(grid), dim3((4 + NP) * 64), p.lds_pad, st, p);
     return hipGetLastError();
 }
 
@@ -513,7 +513,7 @@ void mfma_staged_kernel(const GemmParams p) {
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, bool SPREAD = false, int MI = 32, bool PIN = false>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD, MI, PIN>), dim3(grid), dim3(WM * WN * 64), 0, st, p);
+    hipLaunchKernelGGL((mfma_ring_kernel<T, OUT, BM, BN, BK, WM, WN, S, SPREAD, MI, PIN>), dim3(grid), dim3(WM * WN * 64), p.lds_pad, st, p);
     return hipGetLastError();
 }
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S>
@@ -521,13 +521,13 @@ static hipError_t launch_staged(const GemmParams& p, hipStream_t st) {
     const dim3 grid(p.tiles_m * p.tiles_n), block(WM * WN * 64);
     const bool at = p.a_col != 0, bt = p.b_col == 0;  // contiguous across the LDS rows
     if (!at && !bt)
-        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, false>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, false>), grid, block, p.lds_pad, st, p);
     else if (!at && bt)
-        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, true>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, false, true>), grid, block, p.lds_pad, st, p);
     else if (at && !bt)
-        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, false>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, false>), grid, block, p.lds_pad, st, p);
     else
-        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, true>), grid, block, 0, st, p);
+        hipLaunchKernelGGL((mfma_staged_kernel<T, OUT, BM, BN, BK, WM, WN, S, true, true>), grid, block, p.lds_pad, st, p);
     return hipGetLastError();
 }
 

@@ -222,17 +222,17 @@ void valu_staged_kernel(const GemmParams p) {
 template <int BM, int BN, int BK, int TM, int TN, int S>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
     hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S>), dim3(p.tiles_m * p.tiles_n),
-                       dim3((BM / TM) * (BN / TN)), 0, st, p);
+                       dim3((BM / TM) * (BN / TN)), p.lds_pad, st, p);
     return hipGetLastError();
 }
 template <int BM, int BN, int BK, int TM, int TN, int S>
 static hipError_t launch_staged(const GemmParams& p, hipStream_t st) {
     const dim3 grid(p.tiles_m * p.tiles_n), block((BM / TM) * (BN / TN));
     const bool at = p.a_col != 0, bt = p.b_col != 0;
-    if (!at && !bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, false, false>), grid, block, 0, st, p);
-    else if (!at && bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, false, true>), grid, block, 0, st, p);
-    else if (at && !bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, true, false>), grid, block, 0, st, p);
-    else hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, true, true>), grid, block, 0, st, p);
+    if (!at && !bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, false, false>), grid, block, p.lds_pad, st, p);
+    else if (!at && bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, false, true>), grid, block, p.lds_pad, st, p);
+    else if (at && !bt) hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, true, false>), grid, block, p.lds_pad, st, p);
+    else hipLaunchKernelGGL((valu_staged_kernel<BM, BN, BK, TM, TN, S, true, true>), grid, block, p.lds_pad, st, p);
     return hipGetLastError();
 }
 

@@ -152,7 +152,8 @@ bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
 gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, GemmParams* gp) {
     gemm_opts_t opts = {0, 0, 0, 0};
     if (o) opts = *o;
-    if (opts.flags & ~GEMM_FLAG_NO_XCD_REMAP) return fail(GEMM_ERR_INVALID_ARG, "unknown flags 0x%x", opts.flags);
+    if (opts.flags & ~(GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_EQUAL_LDS))
+        return fail(GEMM_ERR_INVALID_ARG, "unknown flags 0x%x", opts.flags);
     if (opts.nstage < 0 || opts.nstage > GEMM_MAX_NSTAGE) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d out of range", opts.nstage);
     if (opts.kernel < 0 || opts.kernel > GEMM_KERNEL_SCALE) return fail(GEMM_ERR_INVALID_ARG, "kernel %d unknown", opts.kernel);
     if (opts.tile < 0) return fail(GEMM_ERR_INVALID_ARG, "tile %d", opts.tile);
@@ -250,6 +251,13 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     plan->bm = t->bm; plan->bn = t->bn; plan->bk = t->bk;
     plan->threads = t->threads;
     plan->lds_bytes = S * t->stage_bytes;
+    if (opts.flags & GEMM_FLAG_EQUAL_LDS) {
+        int deepest = S;
+        for (int d = GEMM_MAX_NSTAGE; d > S; --d)
+            if ((t->stages & (1 << d)) && d * t->stage_bytes <= kLdsLimit) { deepest = d; break; }
+        gp->lds_pad = (deepest - S) * t->stage_bytes;
+        plan->lds_bytes += gp->lds_pad;
+    }
     gp->tiles_m = (int)cdiv(q.M, t->bm);
     gp->tiles_n = (int)cdiv(q.N, t->bn);
     plan->grid = (int64_t)gp->tiles_m * gp->tiles_n;

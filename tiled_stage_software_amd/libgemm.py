@@ -25,6 +25,7 @@ GEMM_F32, GEMM_BF16, GEMM_F16 = 0, 1, 2
 (GEMM_KERNEL_AUTO, GEMM_KERNEL_VALU_RING, GEMM_KERNEL_VALU_STAGED, GEMM_KERNEL_MFMA_RING,
  GEMM_KERNEL_MFMA_STAGED, GEMM_KERNEL_SCALE) = range(6)
 GEMM_FLAG_NO_XCD_REMAP = 1
+GEMM_FLAG_EQUAL_LDS = 2
 GEMM_MAX_NSTAGE = 5
 
 KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: "mfma_staged", 5: "scale"}
