@@ -121,13 +121,13 @@ def test_plans_for_the_workloads():
     # fp32 256^3 NN -> direct ring, small tile
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (32, 32)
-    # bf16 8192^3 NT -> MFMA ring, 256x128 producer / consumer tile, three slots
+    # bf16 8192^3 NT -> MFMA ring, 256x256 split-copy tile (8 waves), two slots
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and (p.bm, p.bn, p.bk) == (256, 128, 64)
-    assert p.nstage == 3 and p.grid == 32 * 64 and p.lds_bytes <= 163840
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and (p.bm, p.bn, p.bk) == (256, 256, 64)
+    assert p.tile == 23 and p.threads == 512 and p.nstage == 2 and p.grid == 32 * 32 and p.lds_bytes <= 163840
     # f16 MLP shape NT
     s, p = plan(F16, F16, ROW, COL, 16384, 14336, 4096)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 112
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 56
     # bf16 4000x3000x2049 NN, fp32 C: odd K and lda -> staged loader
     s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED

@@ -202,6 +202,8 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, [3, 4], 512, 768, 640),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 13, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
+    ("f16", "f16", ROW, COL, K_MFMA_RING, 21, [1, 2], 512, 768, 448),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 19, [2, 3], 2304, 4352, 320),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
@@ -361,7 +363,7 @@ def _planned_variants():
     out = []
     for kern, dt, la, lb in ((K_MFMA_RING, "bf16", ROW, COL), (K_MFMA_STAGED, "f16", ROW, ROW),
                              (K_VALU_RING, "f32", ROW, ROW), (K_VALU_STAGED, "f32", COL, ROW)):
-        for tile in range(1, 21):
+        for tile in range(1, 27):
             for S in range(1, 6):
                 code = {"f32": 0, "bf16": 1, "f16": 2}[dt]
                 M, N, K = 512, 512, 384
@@ -406,6 +408,7 @@ def test_persistent_tiles_walk_several_tiles_exactly(shape, ts):
 
 EQUAL_LDS = [("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3], 512, 384, 256),
              ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2], 768, 640, 576),
+             ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
              ("bf16", "bf16", ROW, COL, K_MFMA_RING, 3, [1, 2, 3], 384, 256, 320)]
 
 

@@ -304,6 +304,70 @@ void mfma_ring_kernel(const GemmParams p) {
     ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
 }
 
+// ---------------------------------------------------------------- split-copy ring
+// Eight waves, two per SIMD, all multiplying (a 256x256 tile, so a quarter fewer copied
+// bytes per FLOP than the 256x128 producer / consumer tile); only the first NC waves --
+// one per SIMD -- issue and wait for the copies, so when one of them stalls on a copy the
+// other wave of its SIMD keeps the matrix core busy.  Both kinds run the same K-loop
+// template and meet at the same barriers.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool COPY>
+struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN, 32> C;
+    DirectLoader<BM, C::ROWB, NC, true> la;
+    DirectLoader<BN, C::ROWB, NC, true> lb;
+    static constexpr int L = DirectLoader<BM, C::ROWB, NC, true>::IPW + DirectLoader<BN, C::ROWB, NC, true>::IPW;
+    // part `part` of `parts` of the slab's L copies (A's first, then B's)
+    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
+        if (!COPY) return;
+        LDS_AS char* st = this->smem + slot * C::STAGE;
+        constexpr int LA_N = decltype(la)::IPW;
+        const int c0 = part * L / parts, c1 = (part + 1) * L / parts;
+        la.issue(slab, st, c0, c1 < LA_N ? c1 : LA_N);
+        lb.issue(slab, st + C::A_BYTES, c0 > LA_N ? c0 - LA_N : 0, c1 - LA_N);
+    }
+    template <int N>
+    __device__ __forceinline__ void wait_slabs() { if (COPY) wait_vm<N * L>(); }
+    __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    template <int BUF, int HAS, int PARTS>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (L + PARTS - 1) / PARTS : 0>(); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_split_kernel(const GemmParams p) {
+    static constexpr int STAGE = (BM + BN) * BK * 2;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    const int m_keep = tm * BM, n_keep = tn * BN;
+    const int m0 = min(m_keep, p.M - BM);
+    const int n0 = min(n_keep, p.N - BN);
+    if (wave_id() < NC) {
+        SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
+        ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
+        gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+    } else {
+        SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+    }
+}
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false>
+static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
+    const int grid = p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD>), dim3(grid), dim3(WM * WN * 64),
+                       p.lds_pad, st, p);
+    return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- wave-specialised ring
 // Producer / consumer split of the same ring: NP producer waves issue every global->LDS
 // copy and wait for it; 4 consumer waves (2x2, wave tile (BM/2) x (BN/2)) only read
@@ -611,6 +675,21 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             break;
         case 22:  // 256x128x64, 4 consumer waves + 1 producer wave
             if (S == 3) return launch_ws<T, OUT, 256, 128, 64, 3, 1>(p, st);
+            break;
+        case 21:  // 256x256x64, 4x2 waves of 64x128, copies by waves 0-3 only
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 4, 2, 1, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 4, 2, 2, 4>(p, st);
+            break;
+        case 23:  // 256x256x64, 2x4 waves of 128x64, copies by waves 0-3 only
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
+            break;
+        case 24:  // tile 23 with each slab's copies spread over the k-steps
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true>(p, st);
+            break;
+        case 25:  // 256x256x32, 2x4 waves, copies by waves 0-3 spread, deeper ring
+            if (S == 3) return launch_split<T, OUT, 256, 256, 32, 2, 4, 3, 4, true>(p, st);
+            if (S == 4) return launch_split<T, OUT, 256, 256, 32, 2, 4, 4, 4, true>(p, st);
             break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);

@@ -69,11 +69,15 @@ const Tile kMfmaRing[] = {
     {19, 256, 128, 64, 384, S2 | S3, 3, (256 + 128) * 64 * 2},    // tile 18, persistent
     {20, 256, 128, 64, 512, S3, 3, (256 + 128) * 64 * 2},         // tile 17, persistent
     {22, 256, 128, 64, 320, S3, 3, (256 + 128) * 64 * 2},         // 4 consumer + 1 producer wave
+    {21, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // 8 waves, copies by 4 of them
+    {23, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // same, 2x4 waves
+    {24, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, copies spread
+    {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
 };
 // The MFMA ring tile used when none is named for a problem of >= 512 256x256 tiles:
-// 256x128x64, three slots, 2 producer waves feeding 4 consumer waves (the fastest
-// measured on 8192^3 bf16; on par with the 256x256 tiles on the f16 MLP shape).
-constexpr int kMfmaRingDefault = 18;
+// 256x256x64, two slots, eight waves (2x4 of 128x64, two per SIMD) of which one per SIMD
+// issues the copies (the fastest measured on 8192^3 bf16 and on the f16 MLP shape).
+constexpr int kMfmaRingDefault = 23;
 
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
