@@ -143,6 +143,16 @@ def test_ring_requirements_fall_back_to_staged():
         assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED, kw
 
 
+def test_fp32_ring_needs_an_aligned_last_column_tile():
+    # row-major B: the shifted last column tile starts at N - bn, which must be 16-byte aligned
+    s, p = plan(F32, F32, ROW, ROW, 300, 257, 48, ldb=260)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_STAGED
+    s, _ = plan(F32, F32, ROW, ROW, 300, 257, 48, ldb=260, kernel=lg.GEMM_KERNEL_VALU_RING)
+    assert s == lg.GEMM_ERR_UNSUPPORTED
+    s, p = plan(F32, F32, ROW, ROW, 300, 260, 48, kernel=lg.GEMM_KERNEL_VALU_RING)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING
+
+
 def test_lds_budget():
     # 256x256x32 tile: 32 KiB per slot; 4 slots fit, 5 exactly fill 160 KiB but are not built
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=2, nstage=4)

@@ -422,3 +422,30 @@ def test_equal_lds_padding_changes_no_bit(case):
         a = run(p, kernel=kern, tile=tile, nstage=S)
         b = run(p, kernel=kern, tile=tile, nstage=S, flags=lg.GEMM_FLAG_EQUAL_LDS)
         assert torch.equal(a, b)
+
+
+RAGGED_TILES = [(23, 2), (24, 2), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2)]
+
+
+@pytest.mark.parametrize("ts", RAGGED_TILES, ids=lambda t: f"t{t[0]}-s{t[1]}")
+def test_ring_tiles_on_ragged_edges(ts):
+    """M and N that are not multiples of the tile (edge tiles shifted inward, each element
+    stored once), K a few slabs long; exact on small integers, 16-bit and fp32 outputs."""
+    tile, S = ts
+    for (M, N, K, out) in ((300, 700, 192, "bf16"), (513, 257, 320, "f32")):
+        say(f"[ragged] tile={tile} S={S} {M}x{N}x{K} -> {out}")
+        p = problem("bf16", out, M, N, K, ROW, COL, dist="int2", seed=97)
+        got = run(p, kernel=K_MFMA_RING, tile=tile, nstage=S)
+        assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
+
+
+@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1)])
+def test_valu_ring_on_ragged_edges(tile, S):
+    """fp32 direct ring with M and N not multiples of the tile (N a multiple of 4, so the
+    shifted last column tile stays 16-byte aligned; row pitch padded): edge tiles shifted
+    inward, every element stored once, exact."""
+    for (M, N, K, ldb) in ((300, 260, 48, 264), (130, 100, 32, 104)):
+        say(f"[ragged valu] tile={tile} S={S} {M}x{N}x{K} ldb={ldb}")
+        p = problem("f32", "f32", M, N, K, ROW, ROW, dist="int2", seed=101, ldb=ldb)
+        got = run(p, kernel=K_VALU_RING, tile=tile, nstage=S)
+        assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))

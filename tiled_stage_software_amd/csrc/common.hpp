@@ -124,10 +124,12 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
 // Store 4 consecutive C elements (row-major, column n..n+3) of type OUT, with a
-// per-element column predicate when the quad straddles N.  Reads C when beta != 0.
+// per-element column predicate when the quad straddles N or the first column `lo` this
+// tile owns (an edge tile shifted inward starts at a column that need not be a multiple
+// of 4).  Reads C when beta != 0.
 template <int OUT>
-__device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f32x4 v) {
-    const bool full = n + 3 < p.N;
+__device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f32x4 v, int lo = 0) {
+    const bool full = n >= lo && n + 3 < p.N;
     if constexpr (OUT == DT_F32) {
         float* c = reinterpret_cast<float*>(p.C) + m * p.ldc + n;
         const bool vec = full && ((reinterpret_cast<uintptr_t>(c) & 15) == 0);
@@ -141,7 +143,7 @@ __device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f3
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                if (n + j < p.N) c[j] = epi(v[j], p.alpha, p.beta, p.beta != 0.0f ? c[j] : 0.0f);
+                if (n + j >= lo && n + j < p.N) c[j] = epi(v[j], p.alpha, p.beta, p.beta != 0.0f ? c[j] : 0.0f);
         }
     } else {
         constexpr bool bf = OUT == DT_BF16;
@@ -165,7 +167,7 @@ __device__ __forceinline__ void store4(const GemmParams& p, int64_t m, int n, f3
         } else {
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                if (n + j < p.N) {
+                if (n + j >= lo && n + j < p.N) {
                     float o = 0.0f;
                     if (p.beta != 0.0f) o = bf ? bf16_bits_to_f32(c[j]) : f16_bits_to_f32(c[j]);
                     const float r = epi(v[j], p.alpha, p.beta, o);

@@ -166,13 +166,13 @@ struct MfmaCompute {
                     // MI = 32: register group g covers n = 8g + 4*(lane/32) + 0..3;
                     // MI = 16: the single group covers n = 4*(lane/16) + 0..3
                     const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
-                    if (mok && n >= n_keep && n < p.N) {
+                    if (mok && n + 3 >= n_keep && n < p.N) {
                         f32x4 v;
                         v[0] = acc[i][j][4 * g + 0];
                         v[1] = acc[i][j][4 * g + 1];
                         v[2] = acc[i][j][4 * g + 2];
                         v[3] = acc[i][j][4 * g + 3];
-                        store4<OUT>(p, m, n, v);
+                        store4<OUT>(p, m, n, v, n_keep);
                     }
                 }
             }

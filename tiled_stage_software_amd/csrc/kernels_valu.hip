@@ -114,11 +114,11 @@ struct ValuCompute {
 #pragma unroll
             for (int h = 0; h < TN / 4; ++h) {
                 const int n = n0 + 4 * tc + 4 * TGN * h;
-                if (n < n_keep || n >= p.N) continue;
+                if (n + 3 < n_keep || n >= p.N) continue;
                 f32x4 v;
 #pragma unroll
                 for (int j = 0; j < 4; ++j) v[j] = acc[i][4 * h + j];
-                store4<DT_F32>(p, m, n, v);
+                store4<DT_F32>(p, m, n, v, n_keep);
             }
         }
     }

@@ -146,6 +146,13 @@ bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
     if (q.lda % vec || q.ldb % vec) { *why = "leading dimensions not a multiple of 16 bytes"; return false; }
     if (q.K == 0 || q.K % t.bk) { *why = "K not a multiple of the slab depth"; return false; }
     if (q.M < t.bm || q.N < t.bn) { *why = "problem smaller than the tile"; return false; }
+    // The last column tile is shifted inward to start at N - bn; with row-major B (the fp32
+    // ring) that column is the start of each copied 16-byte chunk, so it must be a
+    // multiple of the vector width.  (The MFMA ring shifts only along K-contiguous rows,
+    // whose starts the leading-dimension rule already aligns.)
+    if (!mfma && q.N % t.bn && (q.N - t.bn) % vec) {
+        *why = "last column tile would start off a 16-byte boundary (N not a multiple of 4)"; return false;
+    }
     // per-lane 32-bit offsets span up to one tile of rows (<= 256) of the operand
     if ((q.lda * es) * 256 >= (int64_t(1) << 31) || (q.ldb * es) * 256 >= (int64_t(1) << 31)) {
         *why = "leading dimension too large"; return false;
