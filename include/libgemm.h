@@ -110,6 +110,9 @@ typedef struct gemm_plan {
     int64_t grid;      /* workgroups launched (0 if nothing is launched); for the persistent
                           MFMA ring tiles (19, 20) the number of output tiles, which one
                           workgroup per compute unit walks */
+    int packed;        /* gemm_workspace_size only: bit 0 / bit 1 = A / B is first rewritten
+                          into the workspace (then the fields above describe the multiply of
+                          the rewritten operands, K rounded up to a multiple of 64); else 0 */
 } gemm_plan_t;
 
 /* fp32 A, B, C. */
@@ -140,6 +143,45 @@ gemm_status_t gemm_f16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t
                           float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
                           float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
                           const gemm_opts_t* opts);
+
+/* Same as gemm_bf16_ex / gemm_f16_ex, with a caller-owned device workspace that lets the
+ * direct-to-LDS ring take operands it cannot read in place.  The ring copies 16-byte
+ * chunks of K-contiguous rows straight into LDS, a whole K-slab at a time (the page
+ * "Software Pipelining and Double Buffering", section "Multi-stage pipelines"; the
+ * staged loads of the other kernels take any layout but pass through registers).  When
+ * an operand is N- or M-contiguous (B row-major, A column-major), has a base or pitch
+ * off 16 bytes, or K is not a multiple of 64, that operand is first rewritten into the
+ * workspace as K-contiguous rows of K' = K rounded up to a multiple of 64 elements, the
+ * extra columns zero (they add +0 to every sum), by one bandwidth-bound pass enqueued on
+ * `stream` before the multiply; the ring then runs on the rewritten operands.
+ * workspace: device memory, 256-byte aligned, not overlapping A, B or C; its contents on
+ * entry do not matter and on return are unspecified.  workspace_bytes: its size; the
+ * size needed is given by gemm_workspace_size.  With a NULL or too small workspace, or a
+ * problem the ring runs as it is or cannot run even rewritten (fp32 input, a problem
+ * smaller than the tile, a forced staged kernel), the call is exactly gemm_*_ex.
+ * The result equals that of the ring on the unpadded problem: same k order per output.
+ * Errors: as gemm_*_ex, plus GEMM_ERR_INVALID_ARG for a workspace not 256-byte aligned.
+ * The workspace must stay untouched until the enqueued work has finished. */
+gemm_status_t gemm_bf16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                           float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                           const gemm_opts_t* opts, void* workspace, size_t workspace_bytes);
+gemm_status_t gemm_f16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                          float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                          float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                          const gemm_opts_t* opts, void* workspace, size_t workspace_bytes);
+
+/* Workspace bytes a gemm_*_ws call with these arguments needs in order to rewrite its
+ * operands (0 when it would not rewrite any), and, if plan is not NULL, what that call
+ * launches when given at least that many bytes (gemm_plan_t.packed says which operands
+ * are rewritten).  Host only; pointers are inspected for NULL and alignment, never
+ * dereferenced.  The size is M*K'*2 (A rewritten) plus N*K'*2 (B rewritten), each
+ * rounded up to 256 bytes, K' = K rounded up to a multiple of 64.
+ * Errors: as gemm_plan, GEMM_ERR_INVALID_ARG for a NULL bytes. */
+gemm_status_t gemm_workspace_size(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb,
+                                  int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                  const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
+                                  const gemm_opts_t* opts, size_t* bytes, gemm_plan_t* plan);
 
 /* Validate and choose exactly as the corresponding gemm_*_ex call would, without
  * launching anything (host only; pointers are inspected for NULL and alignment, never

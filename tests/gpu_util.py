@@ -19,9 +19,24 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def gpu_gemm(p: inputs.Problem, ldc: int | None = None, c_fill=None, **opts):
+DT_CODE = {"f32": lg.GEMM_F32, "bf16": lg.GEMM_BF16, "f16": lg.GEMM_F16}
+
+
+def workspace_bytes(p: inputs.Problem, ldc: int, A_ptr: int, B_ptr: int, C_ptr: int, **opts) -> tuple:
+    """(bytes, plan) that gemm_*_ws needs for this problem (gemm_workspace_size)."""
+    s, n, plan = lg.gemm_workspace_size(DT_CODE[p.dtype], DT_CODE[p.out], p.A.layout, p.B.layout, p.M, p.N, p.K,
+                                        p.alpha, A_ptr, p.A.ld, B_ptr, p.B.ld, p.beta, C_ptr, ldc,
+                                        lg._opts(**opts))
+    lg.check(s)
+    return n, plan
+
+
+def gpu_gemm(p: inputs.Problem, ldc: int | None = None, c_fill=None, ws=None, **opts):
     """Run C = alpha*A*B + beta*C0 on the GPU; returns the C storage (CPU tensor, M x ldc)
-    and the status.  c_fill: value the C buffer holds before the call when beta == 0."""
+    and the status.  c_fill: value the C buffer holds before the call when beta == 0.
+    ws: None = gemm_*_ex; "auto" = gemm_*_ws with the workspace gemm_workspace_size asks
+    for (NaN-filled, so that stale bytes would show); an int = a workspace of that many
+    bytes; a device tensor = that workspace."""
     M, N, K = p.M, p.N, p.K
     ldc = ldc or max(N, 1)
     out_dt = inputs.DTYPES[p.out]
@@ -36,9 +51,18 @@ def gpu_gemm(p: inputs.Problem, ldc: int | None = None, c_fill=None, **opts):
     Cd = Cst.to(DEV)
     Ad = p.A.storage.to(DEV) if p.A.storage.numel() else torch.empty(1, dtype=p.A.storage.dtype, device=DEV)
     Bd = p.B.storage.to(DEV) if p.B.storage.numel() else torch.empty(1, dtype=p.B.storage.dtype, device=DEV)
+    wptr, wbytes = 0, 0
+    if ws is not None:
+        if isinstance(ws, torch.Tensor):
+            W, wbytes = ws, ws.numel() * ws.element_size()
+        else:
+            wbytes = int(ws) if ws != "auto" else \
+                workspace_bytes(p, ldc, Ad.data_ptr(), Bd.data_ptr(), Cd.data_ptr(), **opts)[0]
+            W = torch.full((wbytes // 2 + 1,), float("nan"), dtype=torch.bfloat16, device=DEV)
+        wptr = W.data_ptr()
     s = lg.gemm_operands(p.dtype, p.out, p.A.layout, p.B.layout, M, N, K, p.alpha,
                          Ad.data_ptr(), p.A.ld, Bd.data_ptr(), p.B.ld, p.beta, Cd.data_ptr(), ldc,
-                         torch.cuda.current_stream().cuda_stream, **opts)
+                         torch.cuda.current_stream().cuda_stream, ws_ptr=wptr, ws_bytes=wbytes, **opts)
     if s != lg.GEMM_OK:
         raise lg.GemmError(s, lg.gemm_last_error())
     torch.cuda.synchronize()

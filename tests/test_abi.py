@@ -223,3 +223,72 @@ def test_equal_lds_flag_pads_to_the_deepest_ring():
     assert s == 0 and p.lds_bytes == 3 * (256 + 128) * 64 * 2 <= 163840
     s, _ = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, flags=8)
     assert s == lg.GEMM_ERR_INVALID_ARG
+
+
+def ws_size(in_t, c_t, la, lb, M, N, K, alpha=1.0, A=A16, lda=None, B=B16, ldb=None, beta=0.0, C=C16, ldc=None,
+            **opts):
+    lda = lda if lda is not None else (K if la == ROW else M)
+    ldb = ldb if ldb is not None else (N if lb == ROW else K)
+    ldc = ldc if ldc is not None else N
+    o = lg.GemmOpts(opts.get("nstage", 0), opts.get("kernel", 0), opts.get("tile", 0), opts.get("flags", 0)) \
+        if opts else None
+    return lg.gemm_workspace_size(in_t, c_t, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, o)
+
+
+def test_workspace_size_of_the_irregular_workload():
+    # bf16 4000x3000x2049 NN: both operands rewritten, K padded to 2112
+    s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
+    assert s == 0 and p.packed == 3 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.bk in (32, 64)
+    assert n == 4000 * 2112 * 2 + 3000 * 2112 * 2
+    # without a workspace the same call takes the staged kernel
+    s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED and p.packed == 0
+
+
+def test_workspace_size_rewrites_only_what_the_ring_cannot_read():
+    M, N, K = 1024, 768, 512
+    # K-contiguous, aligned, K a multiple of 64: nothing to rewrite
+    s, n, p = ws_size(BF16, BF16, ROW, COL, M, N, K)
+    assert s == 0 and n == 0 and p.packed == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING
+    # A's pitch off 16 bytes: A only
+    s, n, p = ws_size(BF16, BF16, ROW, COL, M, N, K, lda=K + 1)
+    assert s == 0 and p.packed == 1 and n == M * K * 2
+    # A's base off 16 bytes: A only
+    s, n, p = ws_size(F16, F16, ROW, COL, M, N, K, A=A16 + 2)
+    assert s == 0 and p.packed == 1 and n == M * K * 2
+    # B row-major (N-contiguous): B only
+    s, n, p = ws_size(F16, F32, ROW, ROW, M, N, K)
+    assert s == 0 and p.packed == 2 and n == N * K * 2
+    # A column-major: A only
+    s, n, p = ws_size(BF16, F32, COL, COL, M, N, K)
+    assert s == 0 and p.packed == 1 and n == M * K * 2
+    # K tail: both, K rounded up to 64; sizes rounded up to 256 bytes
+    s, n, p = ws_size(BF16, BF16, ROW, COL, 1001, 777, 100)
+    assert s == 0 and p.packed == 3 and n == (-(-1001 * 128 * 2 // 256) * 256) + (-(-777 * 128 * 2 // 256) * 256)
+
+
+def test_workspace_size_zero_where_the_ring_does_not_apply():
+    for kw in (dict(in_t=F32, c_t=F32, la=ROW, lb=ROW),                     # fp32: VALU kernels
+               dict(in_t=BF16, c_t=BF16, la=ROW, lb=ROW, M=100),             # smaller than any ring tile
+               dict(in_t=BF16, c_t=BF16, la=ROW, lb=ROW, kernel=lg.GEMM_KERNEL_MFMA_STAGED),
+               dict(in_t=BF16, c_t=BF16, la=ROW, lb=ROW, K=0, lda=1),        # only scales C
+               dict(in_t=BF16, c_t=BF16, la=ROW, lb=ROW, alpha=0.0)):
+        args = dict(M=1024, N=1024, K=1000)
+        args.update(kw)
+        s, n, p = ws_size(**args)
+        assert s == 0 and n == 0 and p.packed == 0, kw
+    # a forced ring with a layout it cannot read: planned on the rewritten operands
+    s, n, p = ws_size(BF16, BF16, ROW, ROW, 1024, 1024, 1000, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=3)
+    assert s == 0 and p.packed == 3 and p.tile == 3 and n > 0
+
+
+def test_workspace_argument_errors():
+    s, n, p = ws_size(BF16, BF16, ROW, ROW, 1024, 1024, 1000, lda=10)
+    assert s == lg.GEMM_ERR_INVALID_ARG
+    s = lg.load().gemm_workspace_size(BF16, BF16, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, 64,
+                                      None, None, None)
+    assert s == lg.GEMM_ERR_INVALID_ARG
+    # a workspace off 256 bytes is refused before anything is enqueued
+    s = lg.gemm_bf16_ws(ROW, ROW, 1024, 1024, 1000, 1.0, A16, 1000, B16, 1024, 0.0, C16, BF16, 1024, 0, None,
+                        A16 + 16, 1 << 30)
+    assert s == lg.GEMM_ERR_INVALID_ARG and "aligned" in lg.gemm_last_error()

@@ -1,0 +1,125 @@
+// kernels_pack.hip -- repack 16-bit GEMM operands into the layout the direct-to-LDS ring
+// reads: K-contiguous rows, 16-byte aligned, K zero-padded to a whole number of slabs.
+//
+// The ring copies 16-byte chunks straight from global memory into LDS, so it needs both
+// operands K-contiguous with 16-byte aligned rows and K a multiple of the slab depth (the
+// staged kernels take anything, at the cost of a trip through registers).  An operand
+// that breaks one of these -- an N-contiguous B, a row pitch that is not a multiple of 8
+// elements, a K tail -- is rewritten once per call into a workspace; the multiply then
+// runs on the copies.  Zero padding along K adds products 0*0 = +0 to every sum, so the
+// result is that of the unpadded problem.
+//
+// One launch handles up to two jobs (A and B).  Each workgroup owns a 64 x 64 tile of one
+// job's output.  Output row r, column c (c < len_pad, a multiple of 64):
+//   trans = 0: src[r*ld + c]   (the source is already contiguous along K): rows are
+//              copied 16 bytes per lane, coalesced on both sides;
+//   trans = 1: src[c*ld + r]   (contiguous along the other index): the tile goes through
+//              LDS, read along r and written along c, so both global sides stay coalesced.
+// Columns c >= len are written as zeros.  The pass is bound by HBM bandwidth.
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace gemm {
+
+namespace {
+
+constexpr int kPackTile = 64;
+constexpr int kPackPitch = kPackTile + 8;  // LDS row pitch (elements): 144 bytes, 16-byte aligned rows
+
+// 8 consecutive 16-bit source elements starting at element `idx` (any alignment: the
+// target allows unaligned 16-byte global loads).
+__device__ __forceinline__ u32x4 load8(const uint16_t* src, int64_t idx) {
+    u32x4 t;
+    __builtin_memcpy(&t, src + idx, 16);
+    return t;
+}
+
+// Elements idx + e*stride for e < n (the rest +0), packed two per word.
+__device__ __forceinline__ u32x4 load8_partial(const uint16_t* src, int64_t idx, int64_t stride, int n) {
+    u32x4 t = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if (e < n) t[e >> 1] |= (uint32_t)src[idx + e * stride] << ((e & 1) * 16);
+    return t;
+}
+
+__device__ __forceinline__ void pack_rows(const PackJob& j, int r0, int c0) {
+    const int t = threadIdx.x;
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int r = r0 + (t >> 3) + 32 * pass;
+        const int c = c0 + 8 * (t & 7);
+        if (r >= j.rows) continue;
+        const int64_t idx = (int64_t)r * j.ld + c;
+        u32x4 v;
+        if (c + 8 <= j.len) v = load8(j.src, idx);
+        else v = load8_partial(j.src, idx, 1, j.len - c);  // K tail (n <= 0: all zeros)
+        *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c) = v;
+    }
+}
+
+__device__ __forceinline__ void pack_trans(const PackJob& j, int r0, int c0, uint16_t* tile) {
+    const int t = threadIdx.x;
+    // Load: source line c (contiguous along r), 8 consecutive r per lane; store the 8
+    // values as one 16-byte LDS row chunk tile[c - c0][r - r0 ..].
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int cl = (t >> 3) + 32 * pass;
+        const int rl = 8 * (t & 7);
+        const int c = c0 + cl, r = r0 + rl;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (c < j.len) {
+            const int64_t idx = (int64_t)c * j.ld + r;
+            if (r + 8 <= j.rows) v = load8(j.src, idx);
+            else v = load8_partial(j.src, idx, 1, j.rows - r);
+        }
+        *reinterpret_cast<u32x4*>(tile + cl * kPackPitch + rl) = v;
+    }
+    __syncthreads();
+    // Store: output row r, 8 consecutive c per lane, gathered from 8 LDS rows.
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int rl = (t >> 3) + 32 * pass;
+        const int cl = 8 * (t & 7);
+        const int r = r0 + rl;
+        if (r >= j.rows) continue;
+        u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v[e >> 1] |= (uint32_t)tile[(cl + e) * kPackPitch + rl] << ((e & 1) * 16);
+        *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c0 + cl) = v;
+    }
+}
+
+__global__ __launch_bounds__(kPackThreads) void pack_kernel(PackParams p) {
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kPackTile * kPackPitch];
+    int b = blockIdx.x;
+    const int which = b < p.job[0].blocks ? 0 : 1;
+    if (which) b -= p.job[0].blocks;
+    const PackJob& j = p.job[which];
+    const int r0 = (b / j.tiles_c) * kPackTile;
+    const int c0 = (b % j.tiles_c) * kPackTile;
+    if (j.trans) pack_trans(j, r0, c0, tile);
+    else pack_rows(j, r0, c0);
+}
+
+}  // namespace
+
+hipError_t launch_pack(PackParams p, hipStream_t st) {
+    int64_t total = 0;
+    for (int i = 0; i < 2; ++i) {
+        PackJob& j = p.job[i];
+        if (j.rows <= 0) { j.blocks = 0; j.tiles_c = 1; continue; }
+        if (j.len_pad % kPackTile || j.len > j.len_pad) return hipErrorInvalidValue;
+        j.tiles_c = j.len_pad / kPackTile;
+        const int64_t blocks = (int64_t)((j.rows + kPackTile - 1) / kPackTile) * j.tiles_c;
+        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        j.blocks = (int)blocks;
+        total += blocks;
+    }
+    if (total == 0) return hipSuccess;
+    if (total > INT32_MAX) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)total), dim3(kPackThreads), 0, st, p);
+    return hipGetLastError();
+}
+
+}  // namespace gemm

@@ -74,7 +74,7 @@ const Tile kMfmaRing[] = {
     {24, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, copies spread
     {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
 };
-// The MFMA ring tile used when none is named for a problem of >= 512 256x256 tiles:
+// The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles:
 // 256x256x64, two slots, eight waves (2x4 of 128x64, two per SIMD) of which one per SIMD
 // issues the copies (the fastest measured on 8192^3 bf16 and on the f16 MLP shape).
 constexpr int kMfmaRingDefault = 23;
@@ -225,9 +225,12 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
                 t = find_tile(kValuStaged, many ? 1 : 3);
             }
         } else {
+            // The 256x256 tile wins as soon as its tiles cover about half the compute
+            // units (measured on bf16 NT squares: 3072^3, 144 tiles, 908 vs 758 TFLOP/s
+            // for the best smaller tile; 2048^3, 64 tiles, 402 vs 648).
             const Tile* big = find_tile(kMfmaRing, kMfmaRingDefault);
             const Tile* mid = find_tile(kMfmaRing, 3);
-            const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
+            const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 128;
             const Tile* pick = opts.tile ? find_tile(kMfmaRing, opts.tile) : (many ? big : mid);
             if (pick && ring_ok(q, *pick, true, &why)) { kernel = GEMM_KERNEL_MFMA_RING; t = pick; }
             else {
@@ -276,6 +279,21 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     return GEMM_OK;
 }
 
+gemm_status_t launch(int in_type, const gemm_plan_t& plan, const GemmParams& gp, hipStream_t stream) {
+    if (plan.grid == 0) return GEMM_OK;
+    hipError_t e = hipSuccess;
+    switch (plan.kernel) {
+        case GEMM_KERNEL_SCALE: e = gemm::launch_scale(gp, stream); break;
+        case GEMM_KERNEL_VALU_RING: e = gemm::launch_valu_ring(plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_VALU_STAGED: e = gemm::launch_valu_staged(plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_MFMA_RING: e = gemm::launch_mfma_ring(in_type, plan.tile, plan.nstage, gp, stream); break;
+        case GEMM_KERNEL_MFMA_STAGED: e = gemm::launch_mfma_staged(in_type, plan.tile, plan.nstage, gp, stream); break;
+        default: return fail(GEMM_ERR_UNSUPPORTED, "internal: kernel %d", plan.kernel);
+    }
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GEMM_OK;
+}
+
 gemm_status_t run(const Problem& q, const gemm_opts_t* opts, hipStream_t stream) {
     g_err[0] = 0;
     gemm_status_t s = validate(q);
@@ -284,18 +302,93 @@ gemm_status_t run(const Problem& q, const gemm_opts_t* opts, hipStream_t stream)
     GemmParams gp;
     s = choose(q, opts, &plan, &gp);
     if (s != GEMM_OK) return s;
-    if (plan.grid == 0) return GEMM_OK;
-    hipError_t e = hipSuccess;
-    switch (plan.kernel) {
-        case GEMM_KERNEL_SCALE: e = gemm::launch_scale(gp, stream); break;
-        case GEMM_KERNEL_VALU_RING: e = gemm::launch_valu_ring(plan.tile, plan.nstage, gp, stream); break;
-        case GEMM_KERNEL_VALU_STAGED: e = gemm::launch_valu_staged(plan.tile, plan.nstage, gp, stream); break;
-        case GEMM_KERNEL_MFMA_RING: e = gemm::launch_mfma_ring(q.in_type, plan.tile, plan.nstage, gp, stream); break;
-        case GEMM_KERNEL_MFMA_STAGED: e = gemm::launch_mfma_staged(q.in_type, plan.tile, plan.nstage, gp, stream); break;
-        default: return fail(GEMM_ERR_UNSUPPORTED, "internal: kernel %d", plan.kernel);
+    return launch(q.in_type, plan, gp, stream);
+}
+
+// ------------------------------------------------------------------ repacking path
+// A 16-bit problem whose operands the direct ring cannot read as they are (B
+// N-contiguous, a row pitch off 16 bytes, a K tail) is run by first rewriting the
+// offending operands into a caller-supplied workspace: K-contiguous rows of kp elements,
+// kp = K rounded up to kPackK with zeros, which every ring tile divides.
+constexpr int64_t kPackK = 64;
+constexpr int64_t kWsAlign = 256;
+
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+
+struct PackPlan {
+    bool a = false, b = false;  // operand rewritten into the workspace
+    int64_t kp = 0;             // K of the problem the ring runs
+    int64_t a_bytes = 0, b_bytes = 0;  // workspace bytes per operand (multiples of kWsAlign)
+};
+
+// The ring reads this operand in place: K-contiguous (`want` layout), 16-byte aligned
+// base and pitch, and a pitch small enough for its 32-bit per-lane offsets.
+bool operand_direct(const void* p, int layout, int want, int64_t ld) {
+    return layout == want && aligned16(p) && (ld * 2) % 16 == 0 && (ld * 2) * 256 < (int64_t(1) << 31);
+}
+
+// What gemm_*_ws runs: fills *pp (packing, if any) and *plan / *gp for the kernel that
+// multiplies.  ws: the workspace base, or NULL when only planning (then aligned stand-in
+// addresses take the packed operands' place).  Packs only when the operands as given
+// cannot take the ring and the packed problem can; otherwise plans as gemm_*_ex.
+gemm_status_t plan_ws(const Problem& q, const gemm_opts_t* o, void* ws, PackPlan* pp, gemm_plan_t* plan,
+                      GemmParams* gp) {
+    *pp = PackPlan();
+    const int kernel = o ? o->kernel : 0;
+    const int64_t kp = round_up(q.K, kPackK);
+    const bool candidate = q.in_type != gemm::DT_F32 && q.M > 0 && q.N > 0 && q.K > 0 && q.alpha != 0.0f &&
+                           kp <= INT32_MAX && (kernel == 0 || kernel == GEMM_KERNEL_MFMA_RING);
+    if (candidate) {
+        const bool need_a = kp != q.K || !operand_direct(q.A, q.la, GEMM_ROW_MAJOR, q.lda);
+        const bool need_b = kp != q.K || !operand_direct(q.B, q.lb, GEMM_COL_MAJOR, q.ldb);
+        if (need_a || need_b) {
+            Problem r = q;
+            r.K = kp;
+            char* base = static_cast<char*>(ws);
+            const int64_t a_bytes = need_a ? round_up(q.M * kp * 2, kWsAlign) : 0;
+            const int64_t b_bytes = need_b ? round_up(q.N * kp * 2, kWsAlign) : 0;
+            const void* stand_in = reinterpret_cast<const void*>(kWsAlign);
+            if (need_a) { r.A = base ? base : stand_in; r.la = GEMM_ROW_MAJOR; r.lda = kp; }
+            if (need_b) { r.B = base ? base + a_bytes : stand_in; r.lb = GEMM_COL_MAJOR; r.ldb = kp; }
+            if (choose(r, o, plan, gp) == GEMM_OK && plan->kernel == GEMM_KERNEL_MFMA_RING) {
+                pp->a = need_a; pp->b = need_b; pp->kp = kp;
+                pp->a_bytes = a_bytes; pp->b_bytes = b_bytes;
+                plan->packed = (need_a ? 1 : 0) | (need_b ? 2 : 0);
+                return GEMM_OK;
+            }
+            g_err[0] = 0;
+        }
     }
-    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
-    return GEMM_OK;
+    return choose(q, o, plan, gp);
+}
+
+gemm_status_t run_ws(const Problem& q, const gemm_opts_t* opts, void* ws, size_t ws_bytes, hipStream_t stream) {
+    g_err[0] = 0;
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+    if (ws && (reinterpret_cast<uintptr_t>(ws) % kWsAlign))
+        return fail(GEMM_ERR_INVALID_ARG, "workspace must be %lld-byte aligned", (long long)kWsAlign);
+    PackPlan pp;
+    gemm_plan_t plan;
+    GemmParams gp;
+    s = plan_ws(q, opts, ws, &pp, &plan, &gp);
+    if (s != GEMM_OK) return s;
+    if (!(pp.a || pp.b)) return launch(q.in_type, plan, gp, stream);
+    if (!ws || (int64_t)ws_bytes < pp.a_bytes + pp.b_bytes) return run(q, opts, stream);  // too small: as gemm_*_ex
+    gemm::PackParams pk;
+    memset(&pk, 0, sizeof(pk));
+    char* base = static_cast<char*>(ws);
+    if (pp.a) {  // output row m, column k: A[m*lda + k] (row-major) or A[k*lda + m]
+        pk.job[0] = {static_cast<const uint16_t*>(q.A), reinterpret_cast<uint16_t*>(base), q.lda, (int)q.M, (int)q.K,
+                     (int)pp.kp, q.la == GEMM_COL_MAJOR ? 1 : 0, 0, 0};
+    }
+    if (pp.b) {  // output row n, column k: B[n*ldb + k] (column-major) or B[k*ldb + n]
+        pk.job[1] = {static_cast<const uint16_t*>(q.B), reinterpret_cast<uint16_t*>(base + pp.a_bytes), q.ldb,
+                     (int)q.N, (int)q.K, (int)pp.kp, q.lb == GEMM_ROW_MAJOR ? 1 : 0, 0, 0};
+    }
+    hipError_t e = gemm::launch_pack(pk, stream);
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
+    return launch(q.in_type, plan, gp, stream);
 }
 
 // ------------------------------------------------------------------ schedule recorder
@@ -374,6 +467,33 @@ gemm_status_t gemm_f16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t
     return half_entry(gemm::DT_F16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts);
 }
 
+static gemm_status_t half_entry_ws(int in_type, gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K,
+                                   float alpha, const void* A, int64_t lda, const void* B, int64_t ldb, float beta,
+                                   void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                                   const gemm_opts_t* opts, void* workspace, size_t workspace_bytes) {
+    g_err[0] = 0;
+    if (c_type != GEMM_F32 && (int)c_type != in_type)
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered by this entry point", (int)c_type);
+    Problem q{in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    return run_ws(q, opts, workspace, workspace_bytes, stream);
+}
+
+gemm_status_t gemm_bf16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                           const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                           gemm_dtype_t c_type, int64_t ldc, hipStream_t stream, const gemm_opts_t* opts,
+                           void* workspace, size_t workspace_bytes) {
+    return half_entry_ws(gemm::DT_BF16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts,
+                         workspace, workspace_bytes);
+}
+
+gemm_status_t gemm_f16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
+                          const void* A, int64_t lda, const void* B, int64_t ldb, float beta, void* C,
+                          gemm_dtype_t c_type, int64_t ldc, hipStream_t stream, const gemm_opts_t* opts,
+                          void* workspace, size_t workspace_bytes) {
+    return half_entry_ws(gemm::DT_F16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts,
+                         workspace, workspace_bytes);
+}
+
 gemm_status_t gemm_f32(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,
                        const float* A, int64_t lda, const float* B, int64_t ldb, float beta, float* C, int64_t ldc,
                        hipStream_t stream) {
@@ -406,6 +526,30 @@ gemm_status_t gemm_plan(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
     if (s != GEMM_OK) return s;
     GemmParams gp;
     return choose(q, opts, plan, &gp);
+}
+
+gemm_status_t gemm_workspace_size(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb,
+                                  int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                                  const void* B, int64_t ldb, float beta, const void* C, int64_t ldc,
+                                  const gemm_opts_t* opts, size_t* bytes, gemm_plan_t* plan) {
+    g_err[0] = 0;
+    if (!bytes) return fail(GEMM_ERR_INVALID_ARG, "bytes is NULL");
+    *bytes = 0;
+    if (in_type != GEMM_F32 && in_type != GEMM_BF16 && in_type != GEMM_F16)
+        return fail(GEMM_ERR_INVALID_ARG, "in_type %d", (int)in_type);
+    if (in_type == GEMM_F32 ? c_type != GEMM_F32 : (c_type != GEMM_F32 && c_type != in_type))
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered for in_type %d", (int)c_type, (int)in_type);
+    Problem q{(int)in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+    PackPlan pp;
+    gemm_plan_t pl;
+    GemmParams gp;
+    s = plan_ws(q, opts, nullptr, &pp, &pl, &gp);
+    if (s != GEMM_OK) return s;
+    *bytes = (size_t)(pp.a_bytes + pp.b_bytes);
+    if (plan) *plan = pl;
+    return GEMM_OK;
 }
 
 gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,

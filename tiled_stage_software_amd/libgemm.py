@@ -32,7 +32,7 @@ KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: 
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
-           "gemm_plan", "gemm_tune", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string",
+           "gemm_bf16_ws", "gemm_f16_ws", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string",
            "gemm_last_error")
 
 
@@ -44,7 +44,8 @@ class GemmOpts(ctypes.Structure):
 class GemmPlan(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("nstage", ctypes.c_int), ("tile", ctypes.c_int),
                 ("bm", ctypes.c_int), ("bn", ctypes.c_int), ("bk", ctypes.c_int),
-                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("grid", ctypes.c_int64)]
+                ("threads", ctypes.c_int), ("lds_bytes", ctypes.c_int), ("grid", ctypes.c_int64),
+                ("packed", ctypes.c_int)]
 
     def as_dict(self):
         d = {f: getattr(self, f) for f, _ in self._fields_}
@@ -79,8 +80,15 @@ def load():
         for name in ("gemm_bf16", "gemm_f16"):
             getattr(lib, name).argtypes = base + [i32, i64, vp]
             getattr(lib, name + "_ex").argtypes = base + [i32, i64, vp, ctypes.POINTER(GemmOpts)]
-        for name in ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex"):
+            getattr(lib, name + "_ws").argtypes = base + [i32, i64, vp, ctypes.POINTER(GemmOpts), vp,
+                                                          ctypes.c_size_t]
+        for name in ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
+                     "gemm_bf16_ws", "gemm_f16_ws"):
             getattr(lib, name).restype = i32
+        lib.gemm_workspace_size.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
+                                            i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_size_t),
+                                            ctypes.POINTER(GemmPlan)]
+        lib.gemm_workspace_size.restype = i32
         lib.gemm_plan.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                                   ctypes.POINTER(GemmOpts), ctypes.POINTER(GemmPlan)]
         lib.gemm_plan.restype = i32
@@ -133,6 +141,27 @@ def gemm_bf16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, s
 
 def gemm_f16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None) -> int:
     return load().gemm_f16_ex(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts))
+
+
+def gemm_bf16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None,
+                 workspace=0, workspace_bytes=0) -> int:
+    return load().gemm_bf16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts),
+                               workspace, workspace_bytes)
+
+
+def gemm_f16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None,
+                workspace=0, workspace_bytes=0) -> int:
+    return load().gemm_f16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts),
+                              workspace, workspace_bytes)
+
+
+def gemm_workspace_size(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, opts=None):
+    """Returns (status, bytes, GemmPlan of the call given that many bytes)."""
+    n = ctypes.c_size_t(0)
+    plan = GemmPlan()
+    s = load().gemm_workspace_size(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                                   _ref(opts), ctypes.byref(n), ctypes.byref(plan))
+    return s, n.value, plan
 
 
 def gemm_plan(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, opts=None):
@@ -203,9 +232,11 @@ def _layout_of(t, rows, cols):
 
 
 def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, stream=None,
-           nstage: int = 0, kernel: int = 0, tile: int = 0, flags: int = 0):
+           nstage: int = 0, kernel: int = 0, tile: int = 0, flags: int = 0, workspace=None):
     """C = alpha*A@B + beta*C on device tensors (A: M x K, B: K x N, any of the two
-    layouts per operand, C row-major).  Returns C."""
+    layouts per operand, C row-major).  Returns C.  16-bit inputs: `workspace` (a device
+    tensor, 256-byte aligned, at least gemm_workspace_size bytes; "auto" = allocate one
+    with torch) lets the direct ring take operands it cannot read in place."""
     import torch
     if A.dim() != 2 or B.dim() != 2 or A.shape[1] != B.shape[0]:
         raise ValueError(f"shapes {tuple(A.shape)} @ {tuple(B.shape)}")
@@ -235,9 +266,23 @@ def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, 
                         beta, C.data_ptr(), ldc, st, o)
     elif A.dtype in (torch.bfloat16, torch.float16):
         ct = {torch.float32: GEMM_F32, torch.bfloat16: GEMM_BF16, torch.float16: GEMM_F16}[C.dtype]
-        fn = gemm_bf16_ex if A.dtype == torch.bfloat16 else gemm_f16_ex
-        s = fn(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
-               beta, C.data_ptr(), ct, ldc, st, o)
+        if workspace is None:
+            fn = gemm_bf16_ex if A.dtype == torch.bfloat16 else gemm_f16_ex
+            s = fn(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
+                   beta, C.data_ptr(), ct, ldc, st, o)
+        else:
+            if isinstance(workspace, str):
+                if workspace != "auto":
+                    raise ValueError("workspace: a device tensor or 'auto'")
+                it = GEMM_BF16 if A.dtype == torch.bfloat16 else GEMM_F16
+                s, nbytes, _ = gemm_workspace_size(it, ct, la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1],
+                                                   B.data_ptr(), lb[1], beta, C.data_ptr(), ldc, o)
+                check(s)
+                workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+            fn = gemm_bf16_ws if A.dtype == torch.bfloat16 else gemm_f16_ws
+            s = fn(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
+                   beta, C.data_ptr(), ct, ldc, st, o, workspace.data_ptr(),
+                   workspace.numel() * workspace.element_size())
     else:
         raise ValueError(f"unsupported dtype {A.dtype}")
     check(s)
@@ -245,11 +290,15 @@ def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, 
 
 
 def gemm_operands(in_dtype: str, out_dtype: str, la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb,
-                  beta, C_ptr, ldc, stream=0, nstage=0, kernel=0, tile=0, flags=0) -> int:
-    """Dispatch on dtype names ('f32' / 'bf16' / 'f16') with raw pointers."""
+                  beta, C_ptr, ldc, stream=0, nstage=0, kernel=0, tile=0, flags=0, ws_ptr=0, ws_bytes=0) -> int:
+    """Dispatch on dtype names ('f32' / 'bf16' / 'f16') with raw pointers (16-bit inputs
+    with ws_ptr != 0: the workspace entry points)."""
     o = _opts(nstage, kernel, tile, flags)
     if in_dtype == "f32":
         return gemm_f32_ex(la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ldc, stream, o)
     ct = {"f32": GEMM_F32, "bf16": GEMM_BF16, "f16": GEMM_F16}[out_dtype]
+    if ws_ptr:
+        fn = gemm_bf16_ws if in_dtype == "bf16" else gemm_f16_ws
+        return fn(la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ct, ldc, stream, o, ws_ptr, ws_bytes)
     fn = gemm_bf16_ex if in_dtype == "bf16" else gemm_f16_ex
     return fn(la, lb, M, N, K, alpha, A_ptr, lda, B_ptr, ldb, beta, C_ptr, ct, ldc, stream, o)
