@@ -204,6 +204,8 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 21, [1, 2], 512, 768, 448),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 26, [1, 2], 768, 600, 576),
+    ("bf16", "f32", ROW, COL, K_MFMA_RING, 27, [1, 2], 600, 768, 448),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 19, [2, 3], 2304, 4352, 320),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
@@ -363,7 +365,7 @@ def _planned_variants():
     out = []
     for kern, dt, la, lb in ((K_MFMA_RING, "bf16", ROW, COL), (K_MFMA_STAGED, "f16", ROW, ROW),
                              (K_VALU_RING, "f32", ROW, ROW), (K_VALU_STAGED, "f32", COL, ROW)):
-        for tile in range(1, 27):
+        for tile in range(1, 40):
             for S in range(1, 6):
                 code = {"f32": 0, "bf16": 1, "f16": 2}[dt]
                 M, N, K = 512, 512, 384
@@ -424,7 +426,7 @@ def test_equal_lds_padding_changes_no_bit(case):
         assert torch.equal(a, b)
 
 
-RAGGED_TILES = [(23, 2), (24, 2), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2)]
+RAGGED_TILES = [(23, 2), (24, 2), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2), (26, 2), (27, 1)]
 
 
 @pytest.mark.parametrize("ts", RAGGED_TILES, ids=lambda t: f"t{t[0]}-s{t[1]}")

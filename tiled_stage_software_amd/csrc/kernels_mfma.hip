@@ -691,6 +691,14 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 3) return launch_split<T, OUT, 256, 256, 32, 2, 4, 3, 4, true>(p, st);
             if (S == 4) return launch_split<T, OUT, 256, 256, 32, 2, 4, 4, 4, true>(p, st);
             break;
+        case 26:  // 256x192x64, 4x2 waves of 64x96, copies by waves 0-3 only
+            if (S == 1) return launch_split<T, OUT, 256, 192, 64, 4, 2, 1, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 192, 64, 4, 2, 2, 4>(p, st);
+            break;
+        case 27:  // 192x256x64, 2x4 waves of 96x64, copies by waves 0-3 only
+            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
+            break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);
             if (S == 4) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 4, true, 32, true>(p, st);

@@ -43,38 +43,45 @@ __device__ __forceinline__ u32x4 load8_partial(const uint16_t* src, int64_t idx,
     return t;
 }
 
+// Every lane issues all of its loads before its first store: the compiler cannot move
+// a load of src above a store to dst (they might alias), so interleaving them would
+// leave one load in flight per lane.
 __device__ __forceinline__ void pack_rows(const PackJob& j, int r0, int c0) {
     const int t = threadIdx.x;
+    u32x4 v[2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
         const int r = r0 + (t >> 3) + 32 * pass;
         const int c = c0 + 8 * (t & 7);
-        if (r >= j.rows) continue;
         const int64_t idx = (int64_t)r * j.ld + c;
-        u32x4 v;
-        if (c + 8 <= j.len) v = load8(j.src, idx);
-        else v = load8_partial(j.src, idx, 1, j.len - c);  // K tail (n <= 0: all zeros)
-        *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c) = v;
+        if (r >= j.rows) v[pass] = u32x4{0u, 0u, 0u, 0u};
+        else if (c + 8 <= j.len) v[pass] = load8(j.src, idx);
+        else v[pass] = load8_partial(j.src, idx, 1, j.len - c);  // K tail (n <= 0: all zeros)
+    }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+        const int r = r0 + (t >> 3) + 32 * pass;
+        const int c = c0 + 8 * (t & 7);
+        if (r < j.rows) *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c) = v[pass];
     }
 }
 
 __device__ __forceinline__ void pack_trans(const PackJob& j, int r0, int c0, uint16_t* tile) {
     const int t = threadIdx.x;
-    // Load: source line c (contiguous along r), 8 consecutive r per lane; store the 8
-    // values as one 16-byte LDS row chunk tile[c - c0][r - r0 ..].
+    // Load: source line c (contiguous along r), 8 consecutive r per lane; then store the
+    // 8 values as one 16-byte LDS row chunk tile[c - c0][r - r0 ..].
+    u32x4 in[2];
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass) {
-        const int cl = (t >> 3) + 32 * pass;
-        const int rl = 8 * (t & 7);
-        const int c = c0 + cl, r = r0 + rl;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (c < j.len) {
-            const int64_t idx = (int64_t)c * j.ld + r;
-            if (r + 8 <= j.rows) v = load8(j.src, idx);
-            else v = load8_partial(j.src, idx, 1, j.rows - r);
-        }
-        *reinterpret_cast<u32x4*>(tile + cl * kPackPitch + rl) = v;
+        const int c = c0 + (t >> 3) + 32 * pass, r = r0 + 8 * (t & 7);
+        const int64_t idx = (int64_t)c * j.ld + r;
+        if (c >= j.len) in[pass] = u32x4{0u, 0u, 0u, 0u};
+        else if (r + 8 <= j.rows) in[pass] = load8(j.src, idx);
+        else in[pass] = load8_partial(j.src, idx, 1, j.rows - r);
     }
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass)
+        *reinterpret_cast<u32x4*>(tile + ((t >> 3) + 32 * pass) * kPackPitch + 8 * (t & 7)) = in[pass];
     __syncthreads();
     // Store: output row r, 8 consecutive c per lane, gathered from 8 LDS rows.
 #pragma unroll

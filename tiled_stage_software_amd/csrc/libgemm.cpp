@@ -73,6 +73,8 @@ const Tile kMfmaRing[] = {
     {23, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // same, 2x4 waves
     {24, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, copies spread
     {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
+    {26, 256, 192, 64, 512, S1 | S2, 2, (256 + 192) * 64 * 2},    // tile 23's scheme, 4x2 waves of 64x96
+    {27, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64
 };
 // The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles:
 // 256x256x64, two slots, eight waves (2x4 of 128x64, two per SIMD) of which one per SIMD
@@ -85,6 +87,7 @@ const Tile kMfmaStaged[] = {
 };
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
+constexpr int64_t kComputeUnits = 256;  // compute units of the MI355X (planning is host-only)
 
 template <size_t N>
 const Tile* find_tile(const Tile (&t)[N], int id) {
@@ -231,6 +234,18 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
             const Tile* big = find_tile(kMfmaRing, kMfmaRingDefault);
             const Tile* mid = find_tile(kMfmaRing, 3);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 128;
+            if (many) {
+                // One workgroup of these tiles is resident per compute unit, so the grid
+                // runs in ceil(tiles / CUs) rounds of one tile each: take the shape with
+                // the least work per CU, ceil(tiles / CUs) * bm * bn.  Ties keep the
+                // earlier shape (256x256 first; 192x256 measured faster than 256x192).
+                int64_t best = -1;
+                for (int id : {kMfmaRingDefault, 27, 26}) {
+                    const Tile* c = find_tile(kMfmaRing, id);
+                    const int64_t cost = cdiv(cdiv(q.M, c->bm) * cdiv(q.N, c->bn), kComputeUnits) * c->bm * c->bn;
+                    if (best < 0 || cost < best) { best = cost; big = c; }
+                }
+            }
             const Tile* pick = opts.tile ? find_tile(kMfmaRing, opts.tile) : (many ? big : mid);
             if (pick && ring_ok(q, *pick, true, &why)) { kernel = GEMM_KERNEL_MFMA_RING; t = pick; }
             else {
