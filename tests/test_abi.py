@@ -117,7 +117,7 @@ def test_plans_for_the_workloads():
     # fp32 4096^3 NN -> direct ring, 128x64 tile
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (128, 64)
-    assert p.grid == 32 * 64
+    assert p.grid == 32 * 64 and p.tile == 5 and p.threads == 256 and p.nstage == 3
     # fp32 256^3 NN -> direct ring, small tile
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (32, 32)
@@ -128,9 +128,12 @@ def test_plans_for_the_workloads():
     # f16 MLP shape NT
     s, p = plan(F16, F16, ROW, COL, 16384, 14336, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 56
-    # bf16 4000x3000x2049 NN, fp32 C: odd K and lda -> staged loader
+    # bf16 4000x3000x2049 NN, fp32 C: odd K and lda -> staged loader without a workspace;
+    # with one, the 192x256 split-copy tile on the rewritten operands (252 tiles, one round)
     s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED
+    s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.tile == 27 and p.grid == 21 * 12
 
 
 def test_ring_requirements_fall_back_to_staged():

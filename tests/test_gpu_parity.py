@@ -56,6 +56,8 @@ def same_values(a: torch.Tensor, b: torch.Tensor) -> bool:
 
 FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= the tile
     ("f32", "f32", ROW, ROW, K_VALU_RING, 1, 2, 256, 192, 128),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 5, 3, 256, 192, 128),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 6, 2, 256, 192, 128),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 3, 4, 96, 64, 48),
     ("f32", "f32", COL, COL, K_VALU_STAGED, 1, 2, 130, 70, 45),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, 2, 512, 512, 256),
@@ -195,6 +197,8 @@ def test_full_size_small_integers_bit_exact(name):
 
 RING_STAGES = [
     ("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3, 4], 512, 384, 1024),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 5, [1, 2, 3, 4], 512, 384, 1024),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 4, [1, 2, 3, 4], 256, 320, 512),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 3, [1, 2, 3, 4], 96, 64, 160),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, [1, 2, 3, 4], 512, 768, 640),
@@ -243,6 +247,9 @@ def test_xcd_order_does_not_change_results():
 @pytest.mark.parametrize("kern,tile,S,M,N,K,la,lb", [
     (K_VALU_RING, 3, 2, 256, 256, 256, ROW, ROW),
     (K_VALU_RING, 1, 3, 512, 256, 512, ROW, ROW),
+    (K_VALU_RING, 5, 3, 512, 256, 512, ROW, ROW),
+    (K_VALU_RING, 4, 2, 256, 192, 256, ROW, ROW),
+    (K_VALU_RING, 6, 4, 384, 128, 320, ROW, ROW),
     (K_VALU_RING, 2, 1, 192, 128, 64, ROW, ROW),
     (K_VALU_STAGED, 1, 2, 131, 77, 50, COL, COL),
     (K_VALU_STAGED, 3, 1, 45, 33, 19, ROW, COL),
@@ -409,6 +416,7 @@ def test_persistent_tiles_walk_several_tiles_exactly(shape, ts):
 
 
 EQUAL_LDS = [("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3], 512, 384, 256),
+             ("f32", "f32", ROW, ROW, K_VALU_RING, 5, [1, 2, 3], 512, 384, 256),
              ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2], 768, 640, 576),
              ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
              ("bf16", "bf16", ROW, COL, K_MFMA_RING, 3, [1, 2, 3], 384, 256, 320)]
@@ -441,7 +449,7 @@ def test_ring_tiles_on_ragged_edges(ts):
         assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
 
 
-@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1)])
+@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2)])
 def test_valu_ring_on_ragged_edges(tile, S):
     """fp32 direct ring with M and N not multiples of the tile (N a multiple of 4, so the
     shifted last column tile stays 16-byte aligned; row pitch padded): edge tiles shifted

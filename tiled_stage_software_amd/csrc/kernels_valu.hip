@@ -8,8 +8,14 @@
 // buffering of "Matrix multiplication" / section 6 of the multi-stage page).
 //
 // Every accumulator is ONE fp32 fma chain in ascending k starting from +0, whatever the
-// tile, the stage count or the loader: results are bit-identical across variants and
-// equal to a sequential fmaf() loop.
+// tile, the stage count, the k-step width or the loader: results are bit-identical
+// across variants and equal to a sequential fmaf() loop.
+//
+// A k-step covers KW = 4 consecutive k: each lane reads its A rows as whole 16-byte
+// chunks (4 k), which the chunk swizzle spreads over distinct banks for any 8
+// consecutive rows.  With KW = 2 (8-byte halves of a chunk) the 16 rows a wave reads
+// share half the banks, a two-way conflict on every A read (kept as a tile for the
+// comparison).
 //
 // LDS tiles per ring slot: A as [BM rows = m][BK floats = k] (XOR-swizzled 16-byte
 // chunks), B as [BK rows = k][BN floats = n].
@@ -19,18 +25,22 @@
 //   columns n = 4*tc + 4*(BN/TN)*h + j,         h < TN/4, j < 4
 // so the lanes of a wave read consecutive rows (conflict-free through the swizzle) and
 // consecutive 16-byte column groups of B.
+#include <type_traits>
+
 #include "common.hpp"
 #include "loaders.hpp"
 #include "launch.hpp"
 
 namespace gemm {
 
-template <int BM, int BN, int BK, int TM, int TN>
+template <int BM, int BN, int BK, int TM, int TN, int KW = 4>
 struct ValuCompute {
     static constexpr int TGM = BM / TM;  // thread rows
     static constexpr int TGN = BN / TN;  // thread cols
     static constexpr int NT = TGM * TGN;
-    static constexpr int KS = BK / 2;    // k-steps (2 k each) per slab
+    static constexpr int KS = BK / KW;   // k-steps (KW k each) per slab
+    static constexpr int CH = BK / 4;    // 16-byte chunks per A row
+    static_assert(KW == 2 || KW == 4, "k-step of 2 or 4 k");
     static constexpr int A_ROWB = BK * 4;
     static constexpr int B_ROWB = BN * 4;
     static constexpr int A_BYTES = BM * A_ROWB;
@@ -45,10 +55,11 @@ struct ValuCompute {
     static constexpr int NQ = (TGM % 16 == 0) ? 1 : (TGM % 8 == 0 ? 2 : (TGM % 4 == 0 ? 4 : 16));
     static_assert(TM % NQ == 0 || NQ == 1, "rows per thread must cover the swizzle classes evenly");
 
+    typedef typename std::conditional<KW == 4, f32x4, f32x2>::type fa_t;
     float acc[TM][TN];
-    f32x2 fa[2][TM];          // fa[buf][i] = A[m_i][2ks .. 2ks+1]
-    f32x4 fb[2][2][TN / 4];   // fb[buf][kk][h] = B[2ks+kk][n_h .. n_h+3]
-    uint32_t a_addr[NQ][KS / 2];  // LDS byte offset of (row tr + TGM*q, 16-byte chunk c)
+    fa_t fa[2][TM];           // fa[buf][i] = A[m_i][KW*ks .. KW*ks + KW)
+    f32x4 fb[2][KW][TN / 4];  // fb[buf][kk][h] = B[KW*ks + kk][n_h .. n_h+3]
+    uint32_t a_addr[NQ][CH];  // LDS byte offset of (row tr + TGM*q, 16-byte chunk c)
     uint32_t b_col;               // LDS byte offset of column 4*tc of B row 0
     LDS_AS char* smem;
 
@@ -59,7 +70,7 @@ struct ValuCompute {
 #pragma unroll
         for (int q = 0; q < NQ; ++q)
 #pragma unroll
-            for (int c = 0; c < KS / 2; ++c) {
+            for (int c = 0; c < CH; ++c) {
                 const int m = tr + TGM * q;
                 a_addr[q][c] = (uint32_t)(m * A_ROWB + ((c ^ swz<A_CPR>(m)) << 4));
             }
@@ -73,25 +84,25 @@ struct ValuCompute {
     template <int BUF>
     __device__ __forceinline__ void frag(int slot, int ks) {
         LDS_AS const char* st = smem + slot * STAGE;
-        // k = 2ks, 2ks+1 sit in 16-byte chunk ks/2 of the A row, at byte 8*(ks mod 2);
-        // row tr + TGM*i = (row tr + TGM*(i mod NQ)) + TGM*NQ*(i / NQ) rows, whose swizzle
-        // is the same (TGM*NQ is a multiple of 16).
+        // k = KW*ks .. KW*ks + KW - 1 sit in 16-byte chunk (KW*ks)/4 of the A row, at byte
+        // 4*(KW*ks mod 4); row tr + TGM*i = (row tr + TGM*(i mod NQ)) + TGM*NQ*(i / NQ)
+        // rows, whose swizzle is the same (TGM*NQ is a multiple of 16).
 #pragma unroll
         for (int i = 0; i < TM; ++i)
-            fa[BUF][i] = *reinterpret_cast<LDS_AS const f32x2*>(
-                st + a_addr[i % NQ][ks >> 1] + (ks & 1) * 8 + (i / NQ) * (TGM * NQ * A_ROWB));
+            fa[BUF][i] = *reinterpret_cast<LDS_AS const fa_t*>(
+                st + a_addr[i % NQ][(KW * ks) / 4] + ((KW * ks) % 4) * 4 + (i / NQ) * (TGM * NQ * A_ROWB));
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
             for (int h = 0; h < TN / 4; ++h)
                 fb[BUF][kk][h] = *reinterpret_cast<LDS_AS const f32x4*>(
-                    st + b_col + (2 * ks + kk) * B_ROWB + h * (TGN * 16));
+                    st + b_col + (KW * ks + kk) * B_ROWB + h * (TGN * 16));
     }
 
     template <int BUF>
     __device__ __forceinline__ void math() {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
+        for (int kk = 0; kk < KW; ++kk)
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -125,9 +136,9 @@ struct ValuCompute {
 };
 
 // ---------------------------------------------------------------- direct ring kernel
-template <int BM, int BN, int BK, int TM, int TN, int S>
-struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN> {
-    typedef ValuCompute<BM, BN, BK, TM, TN> C;
+template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
+struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN, KW> {
+    typedef ValuCompute<BM, BN, BK, TM, TN, KW> C;
     static constexpr int NW = C::NT / 64;
     typedef DirectLoader<BM, C::A_ROWB, NW, true> LA;    // rows m, k along the row
     typedef DirectLoader<BK, C::B_ROWB, NW, false> LB;   // rows k, n along the row
@@ -154,11 +165,12 @@ struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN> {
     __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
 };
 
-template <int BM, int BN, int BK, int TM, int TN, int S>
+template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) __attribute__((amdgpu_waves_per_eu(
-    occupancy_waves((BM / TM) * (BN / TN), S * ValuCompute<BM, BN, BK, TM, TN>::STAGE, TM * TN >= 64 ? 3 : 4))))
+    occupancy_waves((BM / TM) * (BN / TN), S * ValuCompute<BM, BN, BK, TM, TN>::STAGE,
+                    TM * TN >= 64 ? (KW == 4 ? 2 : 3) : (TM * TN >= 32 ? 3 : 4)))))
 void valu_ring_kernel(const GemmParams p) {
-    typedef ValuRingOps<BM, BN, BK, TM, TN, S> Ops;
+    typedef ValuRingOps<BM, BN, BK, TM, TN, S, KW> Ops;
     __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -178,8 +190,8 @@ void valu_ring_kernel(const GemmParams p) {
 // AT: A column-major (contiguous across its LDS rows m); BT: B column-major (contiguous
 // across its LDS rows k).  Such operands are transposed on their way into LDS.
 template <int BM, int BN, int BK, int TM, int TN, int S, bool AT, bool BT>
-struct ValuStagedOps : ValuCompute<BM, BN, BK, TM, TN> {
-    typedef ValuCompute<BM, BN, BK, TM, TN> C;
+struct ValuStagedOps : ValuCompute<BM, BN, BK, TM, TN, 2> {  // 2-k steps: the staged loads hold registers too
+    typedef ValuCompute<BM, BN, BK, TM, TN, 2> C;
     StagedLoader<BM, BK, 4, C::NT, true, AT> la;    // LDS rows m, cols k
     StagedLoader<BK, BN, 4, C::NT, false, BT> lb;   // LDS rows k, cols n
 
@@ -219,9 +231,9 @@ void valu_staged_kernel(const GemmParams p) {
 }
 
 // ---------------------------------------------------------------- launch tables
-template <int BM, int BN, int BK, int TM, int TN, int S>
+template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
-    hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S>), dim3(p.tiles_m * p.tiles_n),
+    hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S, KW>), dim3(p.tiles_m * p.tiles_n),
                        dim3((BM / TM) * (BN / TN)), p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -236,22 +248,25 @@ static hipError_t launch_staged(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int TM, int TN>
+template <int BM, int BN, int BK, int TM, int TN, int KW = 4>
 static hipError_t ring_stages(int S, const GemmParams& p, hipStream_t st) {
     switch (S) {
-        case 1: return launch_ring<BM, BN, BK, TM, TN, 1>(p, st);
-        case 2: return launch_ring<BM, BN, BK, TM, TN, 2>(p, st);
-        case 3: return launch_ring<BM, BN, BK, TM, TN, 3>(p, st);
-        case 4: return launch_ring<BM, BN, BK, TM, TN, 4>(p, st);
+        case 1: return launch_ring<BM, BN, BK, TM, TN, 1, KW>(p, st);
+        case 2: return launch_ring<BM, BN, BK, TM, TN, 2, KW>(p, st);
+        case 3: return launch_ring<BM, BN, BK, TM, TN, 3, KW>(p, st);
+        case 4: return launch_ring<BM, BN, BK, TM, TN, 4, KW>(p, st);
     }
     return hipErrorInvalidValue;
 }
 
 hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream_t st) {
     switch (tile) {
-        case 1: return ring_stages<128, 64, 16, 8, 8>(nstage, p, st);  // 128 threads
+        case 1: return ring_stages<128, 64, 16, 8, 8, 2>(nstage, p, st);  // 128 threads, 2-k steps (8-byte A reads)
         case 2: return ring_stages<64, 64, 16, 4, 4>(nstage, p, st);   // 256 threads
         case 3: return ring_stages<32, 32, 16, 4, 4>(nstage, p, st);   // 64 threads
+        case 4: return ring_stages<128, 64, 16, 8, 8>(nstage, p, st);  // tile 1 with 4-k steps
+        case 5: return ring_stages<128, 64, 16, 8, 4>(nstage, p, st);  // 256 threads, 8x4 per thread
+        case 6: return ring_stages<128, 64, 16, 4, 8>(nstage, p, st);  // 256 threads, 4x8 per thread
     }
     return hipErrorInvalidValue;
 }

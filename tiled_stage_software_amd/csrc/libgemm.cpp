@@ -39,10 +39,16 @@ constexpr int S1 = 1 << 1, S2 = 1 << 2, S3 = 1 << 3, S4 = 1 << 4;
 
 // Instantiated tiles of each family (must match the launch tables of the kernels).
 const Tile kValuRing[] = {
-    {1, 128, 64, 16, 128, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},
+    {1, 128, 64, 16, 128, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // 8x8 per thread, 2-k steps
     {2, 64, 64, 16, 256, S1 | S2 | S3 | S4, 2, (64 * 16 + 16 * 64) * 4},
     {3, 32, 32, 16, 64, S1 | S2 | S3 | S4, 2, (32 * 16 + 16 * 32) * 4},
+    {4, 128, 64, 16, 128, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // tile 1 with 4-k steps
+    {5, 128, 64, 16, 256, S1 | S2 | S3 | S4, 3, (128 * 16 + 16 * 64) * 4},  // 8x4 per thread
+    {6, 128, 64, 16, 256, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // 4x8 per thread
 };
+// The fp32 ring tile used for problems of >= 512 128x64 tiles: 256 threads of 8x4, 4-k
+// steps, three slots (the fastest measured on fp32 4096^3 NN).
+constexpr int kValuRingDefault = 5;
 const Tile kValuStaged[] = {
     {1, 128, 64, 16, 128, S1 | S2, 2, (128 * 16 + 16 * 64) * 4},
     {3, 32, 32, 16, 64, S1 | S2, 2, (32 * 16 + 16 * 32) * 4},
@@ -218,7 +224,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     if (kernel == 0) {
         // Automatic: the direct ring when the operands allow it, else the staged loader.
         if (!mfma) {
-            const Tile* big = find_tile(kValuRing, 1);
+            const Tile* big = find_tile(kValuRing, kValuRingDefault);
             const Tile* small = find_tile(kValuRing, 3);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
             const Tile* pick = (opts.tile ? find_tile(kValuRing, opts.tile) : (many ? big : small));
@@ -256,7 +262,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     } else {
         int id = opts.tile;
         switch (kernel) {
-            case GEMM_KERNEL_VALU_RING: t = find_tile(kValuRing, id ? id : 1); break;
+            case GEMM_KERNEL_VALU_RING: t = find_tile(kValuRing, id ? id : kValuRingDefault); break;
             case GEMM_KERNEL_VALU_STAGED: t = find_tile(kValuStaged, id ? id : 1); break;
             case GEMM_KERNEL_MFMA_RING: t = find_tile(kMfmaRing, id ? id : kMfmaRingDefault); break;
             case GEMM_KERNEL_MFMA_STAGED: t = find_tile(kMfmaStaged, id ? id : 1); break;
