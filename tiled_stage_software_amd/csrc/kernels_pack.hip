@@ -14,7 +14,8 @@
 //   trans = 0: src[r*ld + c]   (the source is already contiguous along K): rows are
 //              copied 16 bytes per lane, coalesced on both sides;
 //   trans = 1: src[c*ld + r]   (contiguous along the other index): the tile goes through
-//              LDS, read along r and written along c, so both global sides stay coalesced.
+//              LDS, read along r and written along c, so both global sides stay coalesced
+//              (LDS chunks XOR-swizzled, free of bank conflicts on both sides).
 // Columns c >= len are written as zeros.  The pass is bound by HBM bandwidth.
 #include "common.hpp"
 #include "launch.hpp"
@@ -24,7 +25,16 @@ namespace gemm {
 namespace {
 
 constexpr int kPackTile = 64;
-constexpr int kPackPitch = kPackTile + 8;  // LDS row pitch (elements): 144 bytes, 16-byte aligned rows
+
+// LDS tile of the transposing job: row c (64 elements, 8 chunks of 16 bytes) holds the
+// source line c; its chunk q (elements 8q .. 8q+7 along r) sits at chunk position
+// q ^ ((c >> 3) & 7).  The loads write whole rows (8 lanes per 128-byte row); the stores
+// gather one element from 8 consecutive rows per lane, with the 8 lane groups 8 rows
+// apart: the swizzle puts those groups on 8 different chunks, so the 64 lanes hit 32
+// distinct banks.
+__device__ __forceinline__ int tile_at(int c, int r) {
+    return c * kPackTile + 8 * ((r >> 3) ^ ((c >> 3) & 7)) + (r & 7);
+}
 
 // 8 consecutive 16-bit source elements starting at element `idx` (any alignment: the
 // target allows unaligned 16-byte global loads).
@@ -81,7 +91,7 @@ __device__ __forceinline__ void pack_trans(const PackJob& j, int r0, int c0, uin
     }
 #pragma unroll
     for (int pass = 0; pass < 2; ++pass)
-        *reinterpret_cast<u32x4*>(tile + ((t >> 3) + 32 * pass) * kPackPitch + 8 * (t & 7)) = in[pass];
+        *reinterpret_cast<u32x4*>(tile + tile_at((t >> 3) + 32 * pass, 8 * (t & 7))) = in[pass];
     __syncthreads();
     // Store: output row r, 8 consecutive c per lane, gathered from 8 LDS rows.
 #pragma unroll
@@ -92,13 +102,13 @@ __device__ __forceinline__ void pack_trans(const PackJob& j, int r0, int c0, uin
         if (r >= j.rows) continue;
         u32x4 v = {0u, 0u, 0u, 0u};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e >> 1] |= (uint32_t)tile[(cl + e) * kPackPitch + rl] << ((e & 1) * 16);
+        for (int e = 0; e < 8; ++e) v[e >> 1] |= (uint32_t)tile[tile_at(cl + e, rl)] << ((e & 1) * 16);
         *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c0 + cl) = v;
     }
 }
 
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kPackTile * kPackPitch];
+    __shared__ __attribute__((aligned(16))) uint16_t tile[kPackTile * kPackTile];
     int b = blockIdx.x;
     const int which = b < p.job[0].blocks ? 0 : 1;
     if (which) b -= p.job[0].blocks;
