@@ -123,6 +123,121 @@ __device__ __forceinline__ uint16_t f32_to_f16_bits(float x) {
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) { return (float)__builtin_bit_cast(_Float16, b); }
 
+// Old values of 4 consecutive C elements (row-major, column n..n+3) as fp32, for an
+// epilogue with beta != 0; elements outside [lo, N) are not read (0).  Kept separate from
+// the store so that an epilogue can issue the loads of several quads before any store:
+// a load cannot be moved above a store to C that might alias it.
+template <int OUT>
+__device__ __forceinline__ f32x4 load_c4(const GemmParams& p, int64_t m, int n, int lo) {
+    f32x4 o = {0.f, 0.f, 0.f, 0.f};
+    const bool full = n >= lo && n + 3 < p.N;
+    if constexpr (OUT == DT_F32) {
+        const float* c = reinterpret_cast<const float*>(p.C) + m * p.ldc + n;
+        if (full && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
+            o = *reinterpret_cast<const f32x4*>(c);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n + j >= lo && n + j < p.N) o[j] = c[j];
+        }
+    } else {
+        constexpr bool bf = OUT == DT_BF16;
+        const uint16_t* c = reinterpret_cast<const uint16_t*>(p.C) + m * p.ldc + n;
+        if (full && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
+            const u32x2 w = *reinterpret_cast<const u32x2*>(c);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint16_t b = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+                o[j] = bf ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n + j >= lo && n + j < p.N) o[j] = bf ? bf16_bits_to_f32(c[j]) : f16_bits_to_f32(c[j]);
+        }
+    }
+    return o;
+}
+
+// Store out = epi(v, old) for 4 consecutive C elements (columns n..n+3 within [lo, N));
+// `old` holds the values load_c4 read (ignored when beta == 0).
+template <int OUT>
+__device__ __forceinline__ void store_c4(const GemmParams& p, int64_t m, int n, f32x4 v, f32x4 old, int lo) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = epi(v[j], p.alpha, p.beta, old[j]);
+    const bool full = n >= lo && n + 3 < p.N;
+    if constexpr (OUT == DT_F32) {
+        float* c = reinterpret_cast<float*>(p.C) + m * p.ldc + n;
+        if (full && (reinterpret_cast<uintptr_t>(c) & 15) == 0) {
+            *reinterpret_cast<f32x4*>(c) = r;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n + j >= lo && n + j < p.N) c[j] = r[j];
+        }
+    } else {
+        constexpr bool bf = OUT == DT_BF16;
+        uint16_t* c = reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n;
+        uint16_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = bf ? f32_to_bf16_bits(r[j]) : f32_to_f16_bits(r[j]);
+        if (full && (reinterpret_cast<uintptr_t>(c) & 7) == 0) {
+            u32x2 pk;
+            pk[0] = (uint32_t)w[0] | ((uint32_t)w[1] << 16);
+            pk[1] = (uint32_t)w[2] | ((uint32_t)w[3] << 16);
+            *reinterpret_cast<u32x2*>(c) = pk;
+        } else {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                if (n + j >= lo && n + j < p.N) c[j] = w[j];
+        }
+    }
+}
+
+// C rows start on the boundary a whole quad needs (16 bytes for fp32, 8 for 16-bit), so
+// any quad at a column multiple of 4 can move as one vector.
+template <int OUT>
+__device__ __forceinline__ bool c_quads_aligned(const GemmParams& p) {
+    constexpr int QB = OUT == DT_F32 ? 16 : 8;
+    return (reinterpret_cast<uintptr_t>(p.C) % QB) == 0 && (p.ldc * (OUT == DT_F32 ? 4 : 2)) % QB == 0;
+}
+
+// Unpredicated forms for quads known to lie inside C, at a column multiple of 4, with
+// c_quads_aligned(p).
+template <int OUT>
+__device__ __forceinline__ f32x4 load_c4_vec(const GemmParams& p, int64_t m, int n) {
+    if constexpr (OUT == DT_F32) {
+        return *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(p.C) + m * p.ldc + n);
+    } else {
+        const u32x2 w = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(p.C) + m * p.ldc + n);
+        f32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint16_t b = (uint16_t)(w[j >> 1] >> ((j & 1) * 16));
+            o[j] = OUT == DT_BF16 ? bf16_bits_to_f32(b) : f16_bits_to_f32(b);
+        }
+        return o;
+    }
+}
+template <int OUT>
+__device__ __forceinline__ void store_c4_vec(const GemmParams& p, int64_t m, int n, f32x4 v, f32x4 old) {
+    f32x4 r;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) r[j] = epi(v[j], p.alpha, p.beta, old[j]);
+    if constexpr (OUT == DT_F32) {
+        *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(p.C) + m * p.ldc + n) = r;
+    } else {
+        uint16_t w[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) w[j] = OUT == DT_BF16 ? f32_to_bf16_bits(r[j]) : f32_to_f16_bits(r[j]);
+        u32x2 pk;
+        pk[0] = (uint32_t)w[0] | ((uint32_t)w[1] << 16);
+        pk[1] = (uint32_t)w[2] | ((uint32_t)w[3] << 16);
+        *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(p.C) + m * p.ldc + n) = pk;
+    }
+}
+
 // Store 4 consecutive C elements (row-major, column n..n+3) of type OUT, with a
 // per-element column predicate when the quad straddles N or the first column `lo` this
 // tile owns (an edge tile shifted inward starts at a column that need not be a multiple

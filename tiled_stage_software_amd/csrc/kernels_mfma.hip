@@ -155,16 +155,60 @@ struct MfmaCompute {
         const int w = wave_id();
         const int wm = w / WN, wn = w % WN;
         const int lane = lane_id();
+        // Per block row i: with beta != 0, first the old C of all its TN*NR/4 quads (the
+        // loads then overlap), then the stores.  A tile inside C (not shifted, not cut) with
+        // vector-aligned rows takes unpredicated vectors (a wave-uniform choice): the
+        // per-element edge branches would otherwise make the compiler wait between quads.
+        if (m0 == m_keep && n0 == n_keep && m0 + BM <= p.M && n0 + BN <= p.N && c_quads_aligned<OUT>(p)) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) {
+                const int m = m0 + wm * WTM + i * MI + (lane % MI);
+                f32x4 old[TN][NR / 4];
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NR / 4; ++g) old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if (p.beta != 0.0f) {  // one branch around the batch: its loads issue back to back
+#pragma unroll
+                    for (int j = 0; j < TN; ++j)
+#pragma unroll
+                        for (int g = 0; g < NR / 4; ++g)
+                            old[j][g] = load_c4_vec<OUT>(p, m, n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4);
+                }
+#pragma unroll
+                for (int j = 0; j < TN; ++j)
+#pragma unroll
+                    for (int g = 0; g < NR / 4; ++g) {
+                        const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
+                        f32x4 v;
+                        v[0] = acc[i][j][4 * g + 0];
+                        v[1] = acc[i][j][4 * g + 1];
+                        v[2] = acc[i][j][4 * g + 2];
+                        v[3] = acc[i][j][4 * g + 3];
+                        store_c4_vec<OUT>(p, m, n, v, old[j][g]);
+                    }
+            }
+            return;
+        }
 #pragma unroll
         for (int i = 0; i < TM; ++i) {
             const int m = m0 + wm * WTM + i * MI + (lane % MI);
             const bool mok = m >= m_keep && m < p.M;
+            f32x4 old[TN][NR / 4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
+            for (int j = 0; j < TN; ++j)
 #pragma unroll
                 for (int g = 0; g < NR / 4; ++g) {
                     // MI = 32: register group g covers n = 8g + 4*(lane/32) + 0..3;
                     // MI = 16: the single group covers n = 4*(lane/16) + 0..3
+                    const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
+                    old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (p.beta != 0.0f && mok && n + 3 >= n_keep && n < p.N) old[j][g] = load_c4<OUT>(p, m, n, n_keep);
+                }
+#pragma unroll
+            for (int j = 0; j < TN; ++j) {
+#pragma unroll
+                for (int g = 0; g < NR / 4; ++g) {
                     const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
                     if (mok && n + 3 >= n_keep && n < p.N) {
                         f32x4 v;
@@ -172,7 +216,7 @@ struct MfmaCompute {
                         v[1] = acc[i][j][4 * g + 1];
                         v[2] = acc[i][j][4 * g + 2];
                         v[3] = acc[i][j][4 * g + 3];
-                        store4<OUT>(p, m, n, v, n_keep);
+                        store_c4<OUT>(p, m, n, v, old[j][g], n_keep);
                     }
                 }
             }
