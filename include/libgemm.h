@@ -108,7 +108,7 @@ typedef struct gemm_plan {
     int threads;       /* threads per workgroup */
     int lds_bytes;     /* LDS per workgroup */
     int64_t grid;      /* workgroups launched (0 if nothing is launched); for the persistent
-                          MFMA ring tiles (19, 20) the number of output tiles, which one
+                          MFMA ring tiles (19, 20, 28) the number of output tiles, which one
                           workgroup per compute unit walks */
     int packed;        /* gemm_workspace_size only: bit 0 / bit 1 = A / B is first rewritten
                           into the workspace (then the fields above describe the multiply of

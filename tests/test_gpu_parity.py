@@ -207,6 +207,8 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 13, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, [1, 2], 768, 512, 576),
+    ("f16", "f32", ROW, COL, K_MFMA_RING, 29, [1, 2], 600, 768, 448),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 21, [1, 2], 512, 768, 448),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 26, [1, 2], 768, 600, 576),
     ("bf16", "f32", ROW, COL, K_MFMA_RING, 27, [1, 2], 600, 768, 448),
@@ -395,23 +397,24 @@ def test_every_planned_variant_launches_and_matches(v):
 
 # --------------------------------------------------------------- persistent tiles
 
-PERSISTENT = [(19, 2), (19, 3), (20, 3)]
+PERSISTENT = [(19, 2), (19, 3), (20, 3), (28, 2)]
 
 
-@pytest.mark.parametrize("shape", [(4096, 4096, 192), (4100, 3000, 320), (2048, 2560, 128)],
+@pytest.mark.parametrize("shape", [(4096, 4096, 192), (4100, 3000, 320), (2048, 2560, 128), (8192, 4352, 128)],
                          ids=lambda s: "x".join(map(str, s)))
 @pytest.mark.parametrize("ts", PERSISTENT, ids=lambda t: f"t{t[0]}-s{t[1]}")
 def test_persistent_tiles_walk_several_tiles_exactly(shape, ts):
-    """One workgroup per CU walks more tiles than the grid holds (512 and 408 tiles of
-    256x128; 160 fits at once); ragged M / N edges; every element exact on small integers,
-    and the same bits as the non-persistent producer / consumer tile."""
+    """One workgroup per CU walks more tiles than the grid holds (512, 408 and 1088 tiles
+    of 256x128, 544 of 256x256; 160 of 256x128 fit at once); ragged M / N edges; every
+    element exact on small integers, and the same bits as the non-persistent tile of the
+    same scheme (the producer / consumer tile 18, the split-copy tile 23)."""
     M, N, K = shape
     tile, S = ts
     say(f"[persistent] tile={tile} S={S} {M}x{N}x{K}")
     p = problem("bf16", "f32", M, N, K, ROW, COL, dist="int2", seed=83)
     got = run(p, kernel=K_MFMA_RING, tile=tile, nstage=S)
     assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
-    ref = run(p, kernel=K_MFMA_RING, tile=18, nstage=S)
+    ref = run(p, kernel=K_MFMA_RING, tile=23 if tile == 28 else 18, nstage=S)
     assert torch.equal(got, ref)
 
 
@@ -434,7 +437,7 @@ def test_equal_lds_padding_changes_no_bit(case):
         assert torch.equal(a, b)
 
 
-RAGGED_TILES = [(23, 2), (24, 2), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2), (26, 2), (27, 1)]
+RAGGED_TILES = [(23, 2), (24, 2), (24, 1), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2), (26, 2), (27, 1), (29, 2)]
 
 
 @pytest.mark.parametrize("ts", RAGGED_TILES, ids=lambda t: f"t{t[0]}-s{t[1]}")

@@ -80,7 +80,7 @@ def test_identical_to_the_ring_on_operands_packed_by_torch():
     M, N, K = 520, 390, 2049
     Kp = 2112
     p = problem("bf16", "f32", M, N, K, ROW, ROW, dist="normal", alpha=0.5, beta=1.0, seed=7, lda=K)
-    for tile, S in ((0, 0), (23, 2), (3, 2), (18, 3)):
+    for tile, S in ((0, 0), (23, 2), (29, 2), (3, 2), (18, 3)):
         opts = dict(kernel=K_MFMA_RING, tile=tile, nstage=S) if tile else {}
         say(f"[ws torch-packed] tile={tile} S={S}")
         got = run(p, ws="auto", **opts)
@@ -165,7 +165,7 @@ def test_irregular_tail_workload_reduced_whole_matrix():
     assert err_vs_oracle(p, got) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("tile,stages", [(23, (1, 2)), (18, (1, 2, 3)), (3, (1, 2, 3, 4))])
+@pytest.mark.parametrize("tile,stages", [(23, (1, 2)), (29, (1, 2)), (18, (1, 2, 3)), (3, (1, 2, 3, 4))])
 def test_rewritten_operands_bit_identical_across_stage_counts(tile, stages):
     """Ring depth changes no bit on the rewritten-operand path either."""
     p = problem("bf16", "f32", 700, 600, 2049, ROW, ROW, dist="normal", alpha=0.5, beta=1.0, seed=9, lda=2049)

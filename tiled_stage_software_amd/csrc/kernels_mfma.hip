@@ -404,6 +404,99 @@ void mfma_split_kernel(const GemmParams p) {
     }
 }
 
+// Persistent form of the split-copy ring: one workgroup per compute unit walks the tile
+// slots wg, wg + G, wg + 2G, ... (G, the grid, a multiple of 8, so a slot stays on its
+// workgroup's XCD) through ONE ring whose slab index g runs over all its tiles' K-slabs.
+// The copy of the next tile's first slab is issued while the current tile's last slab is
+// multiplied, and the current tile's C is stored between the two (after_slab): the
+// stores drain while the next tile computes, and no tile waits for the ring to fill.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool COPY>
+struct SplitPersistOps : SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, COPY> {
+    typedef SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, COPY> Base;
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN, 32> C;
+    const GemmParams* gp;
+    int numK, wg, G;
+    __device__ __forceinline__ void tile_origin(int j, int& m_keep, int& n_keep, int& m0, int& n0) const {
+        int tm, tn;
+        tile_coords_of(*gp, wg + j * G, tm, tn);
+        m_keep = tm * BM;
+        n_keep = tn * BN;
+        m0 = min(m_keep, gp->M - BM);
+        n0 = min(n_keep, gp->N - BN);
+    }
+    // part `part` of `parts` of the copies of slab g (tile g / numK, K-slab g mod numK)
+    __device__ __forceinline__ void issue(int g, int slot, int part, int parts) {
+        if (!COPY) return;
+        const int j = g / numK, kt = g - j * numK;
+        int mk, nk, m0, n0;
+        tile_origin(j, mk, nk, m0, n0);
+        LDS_AS char* st = this->smem + slot * C::STAGE;
+        constexpr int LA_N = decltype(this->la)::IPW;
+        const int c0 = part * Base::L / parts, c1 = (part + 1) * Base::L / parts;
+        this->la.issue_at(gp->A + ((int64_t)m0 * gp->lda + (int64_t)kt * BK) * 2, st, c0, c1 < LA_N ? c1 : LA_N);
+        this->lb.issue_at(gp->B + ((int64_t)n0 * gp->ldb + (int64_t)kt * BK) * 2, st + C::A_BYTES,
+                          c0 > LA_N ? c0 - LA_N : 0, c1 - LA_N);
+    }
+    // after the last k-step of slab g: if g ends a tile, store it and start the next one
+    template <int OUT>
+    __device__ __forceinline__ void finish_tile(int g) {
+        const int j = g / numK;
+        if (g - j * numK != numK - 1) return;
+        int mk, nk, m0, n0;
+        tile_origin(j, mk, nk, m0, n0);
+        this->template epilogue<OUT>(*gp, m0, n0, mk, nk);
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+#pragma unroll
+            for (int q = 0; q < C::TN; ++q)
+#pragma unroll
+                for (int e = 0; e < C::NR; ++e) this->acc[i][q][e] = 0.0f;
+    }
+};
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool COPY>
+struct SplitPersistOpsOut : SplitPersistOps<T, BM, BN, BK, WM, WN, S, NC, COPY> {
+    __device__ __forceinline__ void after_slab(int g) { this->template finish_tile<OUT>(g); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_splitp_kernel(const GemmParams p) {
+    static constexpr int STAGE = (BM + BN) * BK * 2;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    const int G = gridDim.x, wg = blockIdx.x;
+    const int total = p.tiles_m * p.tiles_n;
+    const int ntiles = wg < total ? (total - wg + G - 1) / G : 0;
+    const int numK = p.K / BK;
+    const int nslabs = ntiles * numK;
+    if (wave_id() < NC) {
+        SplitPersistOpsOut<T, OUT, BM, BN, BK, WM, WN, S, NC, true> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
+        ops.la.init(p.A, p.lda * 2, BK * 2);
+        ops.lb.init(p.B, p.ldb * 2, BK * 2);
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+    } else {
+        SplitPersistOpsOut<T, OUT, BM, BN, BK, WM, WN, S, NC, false> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
+        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+    }
+}
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+static hipError_t launch_splitp(const GemmParams& p, hipStream_t st) {
+    const int total = p.tiles_m * p.tiles_n;
+    // one workgroup per CU (the ring takes most of the LDS); a multiple of 8 keeps each
+    // tile slot on its workgroup's XCD
+    int grid = num_compute_units();
+    grid -= grid & 7;
+    if (grid < 8) grid = 8;
+    if (grid > total) grid = total;
+    hipLaunchKernelGGL((mfma_splitp_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC>), dim3(grid), dim3(WM * WN * 64),
+                       p.lds_pad, st, p);
+    return hipGetLastError();
+}
+
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false>
 static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
@@ -728,7 +821,9 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
             if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
             break;
-        case 24:  // tile 23 with each slab's copies spread over the k-steps
+        case 24:  // tile 23 with each slab's copies spread over the k-steps (S = 1: one slot,
+                  // the slab's copies go out together, as in tile 23)
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true>(p, st);
             if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true>(p, st);
             break;
         case 25:  // 256x256x32, 2x4 waves, copies by waves 0-3 spread, deeper ring
@@ -742,6 +837,13 @@ static hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_
         case 27:  // 192x256x64, 2x4 waves of 96x64, copies by waves 0-3 only
             if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
+            break;
+        case 29:  // tile 27 (192x256) with each slab's copies spread over the k-steps
+            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true>(p, st);
+            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, true>(p, st);
+            break;
+        case 28:  // tile 23, persistent (one workgroup per CU walks several tiles through one ring)
+            if (S == 2) return launch_splitp<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
             break;
         case 16:  // tile 9 (8 waves, 256x256x32, spread) with pinned issue order
             if (S == 3) return launch_ring<T, OUT, 256, 256, 32, 2, 4, 3, true, 32, true>(p, st);

@@ -77,15 +77,19 @@ const Tile kMfmaRing[] = {
     {22, 256, 128, 64, 320, S3, 3, (256 + 128) * 64 * 2},         // 4 consumer + 1 producer wave
     {21, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // 8 waves, copies by 4 of them
     {23, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // same, 2x4 waves
-    {24, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, copies spread
+    {24, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 23, copies spread
     {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
     {26, 256, 192, 64, 512, S1 | S2, 2, (256 + 192) * 64 * 2},    // tile 23's scheme, 4x2 waves of 64x96
     {27, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64
+    {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
+    {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 27, copies spread
 };
-// The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles:
-// 256x256x64, two slots, eight waves (2x4 of 128x64, two per SIMD) of which one per SIMD
-// issues the copies (the fastest measured on 8192^3 bf16 and on the f16 MLP shape).
-constexpr int kMfmaRingDefault = 23;
+// The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles (and
+// the cost model below keeps 256x256): 256x256x64, two slots, eight waves (2x4 of
+// 128x64, two per SIMD) of which one per SIMD issues the copies, each slab's copies
+// spread over its k-steps (the fastest measured on 8192^3 bf16 and on the f16 MLP shape,
+// 2% ahead of issuing them together).
+constexpr int kMfmaRingDefault = 24;
 
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
@@ -246,7 +250,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
                 // the least work per CU, ceil(tiles / CUs) * bm * bn.  Ties keep the
                 // earlier shape (256x256 first; 192x256 measured faster than 256x192).
                 int64_t best = -1;
-                for (int id : {kMfmaRingDefault, 27, 26}) {
+                for (int id : {kMfmaRingDefault, 29, 26}) {
                     const Tile* c = find_tile(kMfmaRing, id);
                     const int64_t cost = cdiv(cdiv(q.M, c->bm) * cdiv(q.N, c->bn), kComputeUnits) * c->bm * c->bn;
                     if (best < 0 || cost < best) { best = cost; big = c; }
