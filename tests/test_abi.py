@@ -117,7 +117,7 @@ def test_plans_for_the_workloads():
     # fp32 4096^3 NN -> direct ring, 128x64 tile
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (128, 64)
-    assert p.grid == 32 * 64 and p.tile == 5 and p.threads == 256 and p.nstage == 3
+    assert p.grid == 32 * 64 and p.tile == 5 and p.threads == 256 and p.nstage == 4
     # fp32 256^3 NN -> direct ring, small tile
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (32, 32)
