@@ -22,6 +22,7 @@ import json
 import os
 import sys
 import time
+from typing import Optional
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -45,8 +46,11 @@ WORKLOAD_NAME = {
 
 
 def kernel_source_hash() -> str:
+    """Hash of the device sources (the .hip kernels and the headers they include); host
+    code that only chooses among kernels is covered by the plan check in traffic_for."""
     h = hashlib.sha256()
-    for f in sorted(glob.glob(os.path.join(ROOT, "tiled_stage_software_amd", "csrc", "*"))):
+    csrc = os.path.join(ROOT, "tiled_stage_software_amd", "csrc")
+    for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
         with open(f, "rb") as fh:
             h.update(os.path.basename(f).encode() + fh.read())
     return h.hexdigest()[:16]
@@ -209,15 +213,18 @@ def cpu_baseline(w: Workload, target_s: float, nthreads: int):
             "seconds": el, "err_vs_device": err}
 
 
-def traffic_for(name: str, src_hash: str, launch_flops: float):
+def traffic_for(name: str, src_hash: str, plan) -> Optional[int]:
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was taken
-    on the current kernel sources (else null)."""
+    on the current device sources and on the kernel / tile / stage count the benchmark
+    launches (else null)."""
     f = os.path.join(ROOT, "profiles", f"traffic_{name}.json")
     if not os.path.exists(f):
         return None
     with open(f) as fh:
         d = json.load(fh)
     if d.get("kernel_source_hash") != src_hash:
+        return None
+    if d.get("plan") != {"kernel": plan.kernel, "tile": plan.tile, "nstage": plan.nstage}:
         return None
     return d.get("bytes_per_launch")
 
@@ -279,7 +286,7 @@ def main():
     }
     rec["roofline"] = {"bound": BOUND[dt], "achieved": round(value, 2), "peak": PEAK[dt], "unit": "TFLOP/s",
                        "frac": round(value / PEAK[dt], 4),
-                       "traffic": traffic_for(args.config, src_hash, w.flops)}
+                       "traffic": traffic_for(args.config, src_hash, plan)}
     if args.only:
         print(json.dumps(rec), flush=True)
         return
@@ -321,12 +328,15 @@ def main():
                 ww.W = saved
                 entry["no_workspace"] = {"kernel": pn.as_dict(), "ms": round(tn, 5),
                                          "tflops": round(ww.flops / (tn * 1e-3) / 1e12, 2)}
-            # the stage / tile tuner's pick for this problem (measured, not modelled; the
-            # tuner times the calls as gemm_*_ex makes them, without a workspace)
-            ts_, best, bms = lg.gemm_tune(DT_CODE[ww.p.dtype], DT_CODE[ww.p.out], ww.p.A.layout, ww.p.B.layout,
-                                          ww.p.M, ww.p.N, ww.p.K, ww.p.alpha, ww.A.data_ptr(), ww.p.A.ld,
-                                          ww.B.data_ptr(), ww.p.B.ld, ww.p.beta, ww.C.data_ptr(), ww.p.N,
-                                          ww.stream.cuda_stream, reps=200 if name == "c1" else 10)
+            # the stage / tile tuner's pick for this problem (measured, not modelled)
+            targs = (DT_CODE[ww.p.dtype], DT_CODE[ww.p.out], ww.p.A.layout, ww.p.B.layout, ww.p.M, ww.p.N,
+                     ww.p.K, ww.p.alpha, ww.A.data_ptr(), ww.p.A.ld, ww.B.data_ptr(), ww.p.B.ld, ww.p.beta,
+                     ww.C.data_ptr(), ww.p.N, ww.stream.cuda_stream)
+            if ww.W is not None:   # timed as the workspace call the benchmark makes
+                ts_, best, bms = lg.gemm_tune_ws(*targs, workspace=ww.W.data_ptr(), workspace_bytes=ww.W.numel(),
+                                                 reps=10)
+            else:
+                ts_, best, bms = lg.gemm_tune(*targs, reps=200 if name == "c1" else 10)
             lg.check(ts_)
             entry["tuned"] = {"kernel": best.kernel, "tile": best.tile, "nstage": best.nstage, "ms": round(bms, 5),
                               "tflops": round(ww.flops / (bms * 1e-3) / 1e12, 2)}

@@ -212,6 +212,18 @@ gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
                         const void* B, int64_t ldb, float beta, void* C, int64_t ldc, hipStream_t stream,
                         int reps, gemm_opts_t* best, float* best_ms);
 
+/* gemm_tune for the workspace entry points (16-bit inputs): the candidates are every
+ * variant a gemm_bf16_ws / gemm_f16_ws call with this workspace accepts -- ring variants
+ * on rewritten operands that fit in `workspace_bytes` included -- each timed as that call
+ * (the rewrite counted); pass *best to the same call.  Arguments as gemm_tune plus the
+ * workspace (as in gemm_*_ws; its contents afterwards are unspecified).
+ * Errors: as gemm_tune, GEMM_ERR_INVALID_ARG for fp32 input or a workspace not 256-byte
+ * aligned. */
+gemm_status_t gemm_tune_ws(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb,
+                           int64_t M, int64_t N, int64_t K, float alpha, const void* A, int64_t lda,
+                           const void* B, int64_t ldb, float beta, void* C, int64_t ldc, hipStream_t stream,
+                           void* workspace, size_t workspace_bytes, int reps, gemm_opts_t* best, float* best_ms);
+
 /* The K-loop protocol of a kernel family, as the event list its mainloop executes
  * (host only, for checking the pipeline on the CPU).  Each event is 4 ints
  * {type, slab, slot, arg}:

@@ -1,6 +1,7 @@
 """C ABI checks that need no GPU: the library loads, exports what include/libgemm.h
 declares, rejects bad arguments before launching anything, and plans the kernel the
 problem calls for."""
+import ctypes
 import os
 import re
 import subprocess
@@ -294,4 +295,12 @@ def test_workspace_argument_errors():
     # a workspace off 256 bytes is refused before anything is enqueued
     s = lg.gemm_bf16_ws(ROW, ROW, 1024, 1024, 1000, 1.0, A16, 1000, B16, 1024, 0.0, C16, BF16, 1024, 0, None,
                         A16 + 16, 1 << 30)
+    assert s == lg.GEMM_ERR_INVALID_ARG and "aligned" in lg.gemm_last_error()
+    # the workspace tuner refuses fp32 input and a misaligned workspace before timing anything
+    best, ms = lg.GemmOpts(), ctypes.c_float(0.0)
+    s = lg.load().gemm_tune_ws(F32, F32, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, 64, None,
+                               A16, 1 << 20, 2, ctypes.byref(best), ctypes.byref(ms))
+    assert s == lg.GEMM_ERR_INVALID_ARG
+    s = lg.load().gemm_tune_ws(BF16, BF16, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, 64, None,
+                               A16 + 16, 1 << 20, 2, ctypes.byref(best), ctypes.byref(ms))
     assert s == lg.GEMM_ERR_INVALID_ARG and "aligned" in lg.gemm_last_error()

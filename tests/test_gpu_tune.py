@@ -41,3 +41,29 @@ def test_tune_empty_problem_reports_default():
     s, best, ms = lg.gemm_tune(lg.GEMM_BF16, lg.GEMM_BF16, inputs.ROW, inputs.COL, 0, 16, 16, 1.0, d, 16, d, 16,
                                0.0, d, 16, 0, reps=2)
     assert s == lg.GEMM_OK and ms == 0.0
+
+
+def test_tune_with_a_workspace_times_the_workspace_call():
+    """bf16 NN with a K tail: without a workspace only the staged kernel can run; with one
+    the tuner also times ring variants on the rewritten operands, and its pick, passed to
+    gemm_bf16_ws with the same workspace, is exact on small integers."""
+    M, N, K = 700, 600, 300
+    say("[tune ws]")
+    cfg = dict(dtype="bf16", out="f32", M=M, N=N, K=K, la=inputs.ROW, lb=inputs.ROW, dist="int2", std=1.0,
+               alpha=1.0, beta=0.0, index=9)
+    p = inputs.make_problem(cfg)
+    A, B = p.A.storage.to(DEV), p.B.storage.to(DEV)
+    C = torch.zeros(M * N, dtype=torch.float32, device=DEV)
+    args = (lg.GEMM_BF16, lg.GEMM_F32, p.A.layout, p.B.layout, M, N, K, 1.0, A.data_ptr(), p.A.ld, B.data_ptr(),
+            p.B.ld, 0.0, C.data_ptr(), N)
+    s, n, _ = lg.gemm_workspace_size(*args)
+    assert s == lg.GEMM_OK and n > 0
+    W = torch.empty(n, dtype=torch.uint8, device=DEV)
+    st = torch.cuda.current_stream().cuda_stream
+    s, best, ms = lg.gemm_tune_ws(*args, st, W.data_ptr(), n, reps=3)
+    assert s == lg.GEMM_OK and ms > 0.0, lg.gemm_last_error()
+    s, best0, _ = lg.gemm_tune(*args, st, reps=3)
+    assert s == lg.GEMM_OK and best0.kernel == lg.GEMM_KERNEL_MFMA_STAGED
+    Cst, ldc = gpu_gemm(p, ws=W, nstage=best.nstage, kernel=best.kernel, tile=best.tile)
+    got = c_logical(Cst, M, N, ldc).double().numpy()
+    assert np.array_equal(got, expected_rounded(oracle_ref(p), "f32"))

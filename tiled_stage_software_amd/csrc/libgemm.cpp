@@ -577,10 +577,16 @@ gemm_status_t gemm_workspace_size(gemm_dtype_t in_type, gemm_dtype_t c_type, gem
     return GEMM_OK;
 }
 
-gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
-                        int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
-                        float beta, void* C, int64_t ldc, hipStream_t stream, int reps, gemm_opts_t* best,
-                        float* best_ms) {
+}  // extern "C"
+
+namespace {
+
+// The tuner behind gemm_tune / gemm_tune_ws: every (family, tile, stage count) that the
+// call with this workspace (NULL: none) would accept, timed as that call.
+gemm_status_t tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
+                   int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                   float beta, void* C, int64_t ldc, hipStream_t stream, void* ws, size_t ws_bytes, int reps,
+                   gemm_opts_t* best, float* best_ms) {
     g_err[0] = 0;
     if (!best || !best_ms) return fail(GEMM_ERR_INVALID_ARG, "best / best_ms is NULL");
     if (reps < 1 || reps > 100000) return fail(GEMM_ERR_INVALID_ARG, "reps %d", reps);
@@ -588,11 +594,14 @@ gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
         return fail(GEMM_ERR_INVALID_ARG, "in_type %d", (int)in_type);
     if (in_type == GEMM_F32 ? c_type != GEMM_F32 : (c_type != GEMM_F32 && c_type != in_type))
         return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered for in_type %d", (int)c_type, (int)in_type);
+    if (ws && (reinterpret_cast<uintptr_t>(ws) % kWsAlign))
+        return fail(GEMM_ERR_INVALID_ARG, "workspace must be %lld-byte aligned", (long long)kWsAlign);
     Problem q{(int)in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
     gemm_status_t s = validate(q);
     if (s != GEMM_OK) return s;
 
-    // the candidates: every (family, tile, stage count) the planner accepts for q
+    // the candidates: every (family, tile, stage count) the planner accepts for q (with
+    // the workspace: also ring variants on the rewritten operands that fit in it)
     struct Cand { int kernel, tile, nstage; };
     std::vector<Cand> cands;
     const bool mfma = in_type != GEMM_F32;
@@ -610,7 +619,14 @@ gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
                 gemm_opts_t o = {S, fam, tab[t].id, 0};
                 gemm_plan_t pl;
                 GemmParams gp;
-                if (choose(q, &o, &pl, &gp) == GEMM_OK && pl.grid > 0) cands.push_back({fam, tab[t].id, S});
+                PackPlan pp;
+                if (ws) {
+                    if (plan_ws(q, &o, ws, &pp, &pl, &gp) == GEMM_OK && pl.grid > 0 &&
+                        pp.a_bytes + pp.b_bytes <= (int64_t)ws_bytes)
+                        cands.push_back({fam, tab[t].id, S});
+                } else if (choose(q, &o, &pl, &gp) == GEMM_OK && pl.grid > 0) {
+                    cands.push_back({fam, tab[t].id, S});
+                }
             }
     }
     g_err[0] = 0;
@@ -631,10 +647,11 @@ gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
     gemm_status_t result = GEMM_OK;
     for (const Cand& c : cands) {
         gemm_opts_t o = {c.nstage, c.kernel, c.tile, 0};
-        s = run(q, &o, stream);                      // warm-up (code load, caches)
+        auto call = [&]() { return ws ? run_ws(q, &o, ws, ws_bytes, stream) : run(q, &o, stream); };
+        s = call();                      // warm-up (code load, caches)
         if (s != GEMM_OK) { result = s; break; }
         hipError_t he = hipEventRecord(e0, stream);
-        for (int r = 0; r < reps && s == GEMM_OK; ++r) s = run(q, &o, stream);
+        for (int r = 0; r < reps && s == GEMM_OK; ++r) s = call();
         if (s != GEMM_OK) { result = s; break; }
         if (he == hipSuccess) he = hipEventRecord(e1, stream);
         if (he == hipSuccess) he = hipEventSynchronize(e1);
@@ -649,6 +666,30 @@ gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t
     if (result != GEMM_OK) return result;
     *best_ms = best_t;
     return GEMM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_tune(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
+                        int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                        float beta, void* C, int64_t ldc, hipStream_t stream, int reps, gemm_opts_t* best,
+                        float* best_ms) {
+    return tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, nullptr, 0, reps,
+                best, best_ms);
+}
+
+gemm_status_t gemm_tune_ws(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layout_t la, gemm_layout_t lb, int64_t M,
+                           int64_t N, int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                           float beta, void* C, int64_t ldc, hipStream_t stream, void* workspace,
+                           size_t workspace_bytes, int reps, gemm_opts_t* best, float* best_ms) {
+    if (in_type == GEMM_F32) {
+        g_err[0] = 0;
+        return fail(GEMM_ERR_INVALID_ARG, "gemm_tune_ws takes 16-bit inputs");
+    }
+    return tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, workspace,
+                workspace_bytes, reps, best, best_ms);
 }
 
 int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity) {

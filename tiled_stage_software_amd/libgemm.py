@@ -32,7 +32,7 @@ KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: 
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
-           "gemm_bf16_ws", "gemm_f16_ws", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string",
+           "gemm_bf16_ws", "gemm_f16_ws", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_tune_ws", "gemm_schedule", "gemm_pipe_copy", "gemm_status_string",
            "gemm_last_error")
 
 
@@ -97,6 +97,10 @@ def load():
         lib.gemm_tune.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
                                   vp, i32, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_float)]
         lib.gemm_tune.restype = i32
+        lib.gemm_tune_ws.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp, i64,
+                                     vp, vp, ctypes.c_size_t, i32, ctypes.POINTER(GemmOpts),
+                                     ctypes.POINTER(ctypes.c_float)]
+        lib.gemm_tune_ws.restype = i32
         lib.gemm_pipe_copy.argtypes = [vp, vp, i64, i32, vp]
         lib.gemm_pipe_copy.restype = i32
         lib.gemm_status_string.argtypes = [i32]
@@ -189,6 +193,16 @@ def gemm_tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, 
     ms = ctypes.c_float(0.0)
     s = load().gemm_tune(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream, reps,
                          ctypes.byref(best), ctypes.byref(ms))
+    return s, best, ms.value
+
+
+def gemm_tune_ws(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0,
+                 workspace=0, workspace_bytes=0, reps=10):
+    """gemm_tune for the workspace entry points: (status, GemmOpts, ms per call)."""
+    best = GemmOpts()
+    ms = ctypes.c_float(0.0)
+    s = load().gemm_tune_ws(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream,
+                            workspace, workspace_bytes, reps, ctypes.byref(best), ctypes.byref(ms))
     return s, best, ms.value
 
 
