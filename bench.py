@@ -181,28 +181,65 @@ def pipe_copy_control(dev, mib: int = 1024, reps: int = 20):
             "nstage": out, "copy_exact": ok, "hbm_peak_GB/s": 8000}
 
 
+def h2d_staging_control(dev, mib: int = 256, chunk_mib: int = 4, reps: int = 3):
+    """Host-to-device copy of `mib` MiB of ordinary (pageable) host memory through the
+    page-locked staging ring of gemm_h2d_staged, per slot count (wall clock: the call
+    returns once its copies are done), and torch's own pageable copy for context."""
+    n = mib << 20
+    chunk = chunk_mib << 20
+    src = np.random.default_rng(0).integers(0, 256, n, dtype=np.uint8)
+    dst = torch.empty(n, dtype=torch.uint8, device=dev)
+    st = torch.cuda.current_stream(dev).cuda_stream
+    out = {}
+    for S in (1, 2, 3, 4):
+        staging = torch.empty(S * chunk, dtype=torch.uint8, pin_memory=True)
+        lg.check(lg.gemm_h2d_staged(dst.data_ptr(), src.ctypes.data, n, staging.data_ptr(), chunk, S, st))
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            lg.check(lg.gemm_h2d_staged(dst.data_ptr(), src.ctypes.data, n, staging.data_ptr(), chunk, S, st))
+        el = (time.perf_counter() - t0) / reps
+        out[str(S)] = {"ms": round(el * 1e3, 3), "GB/s": round(n / el / 1e9, 2)}
+        del staging
+    ok = bool(np.array_equal(dst.cpu().numpy(), src))
+    host = torch.from_numpy(src)
+    host.to(dev)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        host.to(dev)
+    torch.cuda.synchronize()
+    ref = n / ((time.perf_counter() - t0) / reps) / 1e9
+    del dst
+    return {"what": f"{mib} MiB pageable host -> device through nStage page-locked slots of {chunk_mib} MiB",
+            "nstage": out, "copy_exact": ok, "torch_pageable_copy_GB/s": round(ref, 2)}
+
+
 def cpu_baseline(w: Workload, target_s: float, nthreads: int):
     """Time the oracle (as it stands) on a bounded row sample of the workload on the host
     cores, and check the device result on the same rows."""
     from oracle import oracle
     p = w.p
     la, lb = p.A.layout == inputs.COL, p.B.layout == inputs.COL
-    # probe with one row per thread, then size the sample to ~target_s seconds
+    # batches of rows spread over the whole matrix (a stride-permuted order), run until
+    # about target_s seconds of oracle time have been spent
     threads = oracle.max_threads(nthreads)
-    probe_rows = np.linspace(0, p.M - 1, min(p.M, threads)).astype(np.int64).tolist()
-    dt = 1e-4
-    for _ in range(2):  # the first pass also starts the thread pool: time the second
+    # the operands widened to fp64 once (exact), so each batch times the products only
+    a64 = p.A.storage.double().numpy()
+    b64 = p.B.storage.double().numpy()
+    c64 = None if p.C0 is None else p.C0.storage.double().numpy()
+    order = np.argsort((np.arange(p.M, dtype=np.int64) * 2654435761) % (1 << 32), kind="stable")
+    batch = max(threads * 4, 1)
+    rows, parts, el = [], [], 0.0
+    for b0 in range(0, p.M, batch):
+        chunk = sorted(order[b0:b0 + batch].tolist())
         t0 = time.perf_counter()
-        oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
-                        None if p.C0 is None else p.C0.storage, p.N, rows=probe_rows, nthreads=nthreads)
-        dt = max(time.perf_counter() - t0, 1e-4)
-    n = int(target_s / dt * len(probe_rows))
-    n = max(min(p.M, threads), min(p.M, n))
-    rows = sorted(set(np.linspace(0, p.M - 1, n).astype(np.int64).tolist()))
-    t0 = time.perf_counter()
-    ref = oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, p.A.storage, p.A.ld, p.B.storage, p.B.ld, p.beta,
-                          None if p.C0 is None else p.C0.storage, p.N, rows=rows, nthreads=nthreads)
-    el = time.perf_counter() - t0
+        parts.append(oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, a64, p.A.ld, b64, p.B.ld, p.beta, c64, p.N,
+                                     rows=chunk, nthreads=nthreads))
+        el += time.perf_counter() - t0
+        rows += chunk
+        if el >= target_s:
+            break
+    ref = np.concatenate(parts, axis=0)
     flops = 2.0 * len(rows) * p.N * p.K
     # device check on the same rows (fresh result, C restored first when beta != 0)
     w.reset_c()
@@ -348,6 +385,7 @@ def main():
                 torch.cuda.empty_cache()
         rec["workloads"] = sweep
         rec["negative_control"] = pipe_copy_control(dev)
+        rec["h2d_staging"] = h2d_staging_control(dev)
 
     if not args.no_cpu_baseline:
         w.reset_c()

@@ -255,6 +255,24 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
  * (nstage), GEMM_ERR_HIP (launch). */
 gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nstage, hipStream_t stream);
 
+/* dst[0, bytes) = src[0, bytes) from ordinary (pageable) host memory to the device,
+ * staged through a ring of `nstage` page-locked slots of `chunk_bytes` each: the CPU
+ * copies chunk c into slot c mod nstage while the DMA engine moves the chunks already
+ * staged; a slot is refilled only after the DMA that read it has completed (one event per
+ * slot).  It is the host-side form of the same ring the kernels run, the one the page
+ * "Asynchronous data movement" (CUDA Handbook ch. 17, the paragraph comparing cp.async
+ * with CPU/GPU overlap) recalls for pageable copies: with one slot, filling and draining
+ * alternate; with two or more they overlap.
+ * dst: device memory; src: host memory, not overlapping the staging ring; staging:
+ * page-locked host memory (hipHostMalloc), at least nstage * chunk_bytes bytes; nstage
+ * 1..4; chunk_bytes >= 1 (the last chunk may be shorter).  The DMAs are enqueued on
+ * `stream`; the call returns when all of them have completed (the staging memory is then
+ * free again).  Creates and destroys up to 4 HIP events.
+ * Errors: GEMM_ERR_INVALID_ARG (sizes, NULL, overlap), GEMM_ERR_UNSUPPORTED (nstage),
+ * GEMM_ERR_HIP (a copy, an event or a wait failed). */
+gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
+                              int nstage, hipStream_t stream);
+
 const char* gemm_status_string(gemm_status_t status);
 
 /* Thread-local description of the last non-OK status on this thread ("" if none). */

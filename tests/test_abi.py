@@ -304,3 +304,16 @@ def test_workspace_argument_errors():
     s = lg.load().gemm_tune_ws(BF16, BF16, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, 64, None,
                                A16 + 16, 1 << 20, 2, ctypes.byref(best), ctypes.byref(ms))
     assert s == lg.GEMM_ERR_INVALID_ARG and "aligned" in lg.gemm_last_error()
+
+
+def test_h2d_staged_rejects_bad_arguments_before_copying():
+    H = 0x40000  # fake addresses: every case fails before anything is touched
+    for args, want in (((A16, H, -1, H + (1 << 20), 4096, 2), lg.GEMM_ERR_INVALID_ARG),
+                       ((A16, H, 8192, H + (1 << 20), 0, 2), lg.GEMM_ERR_INVALID_ARG),
+                       ((A16, H, 8192, H + (1 << 20), 4096, 0), lg.GEMM_ERR_UNSUPPORTED),
+                       ((A16, H, 8192, H + (1 << 20), 4096, 5), lg.GEMM_ERR_UNSUPPORTED),
+                       ((0, H, 8192, H + (1 << 20), 4096, 2), lg.GEMM_ERR_INVALID_ARG),
+                       ((A16, H, 8192, 0, 4096, 2), lg.GEMM_ERR_INVALID_ARG),
+                       ((A16, H, 8192, H + 4096, 4096, 2), lg.GEMM_ERR_INVALID_ARG)):  # src overlaps the ring
+        assert lg.gemm_h2d_staged(*args) == want, args
+    assert lg.gemm_h2d_staged(A16, H, 0, H + (1 << 20), 4096, 2) == lg.GEMM_OK   # nothing to copy

@@ -747,6 +747,54 @@ gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nsta
     return GEMM_OK;
 }
 
+gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
+                              int nstage, hipStream_t stream) {
+    g_err[0] = 0;
+    if (bytes < 0) return fail(GEMM_ERR_INVALID_ARG, "bytes %lld < 0", (long long)bytes);
+    if (nstage < 1 || nstage > 4) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d: the staging ring has 1..4 slots", nstage);
+    if (chunk_bytes < 1) return fail(GEMM_ERR_INVALID_ARG, "chunk_bytes %lld < 1", (long long)chunk_bytes);
+    if (bytes == 0) return GEMM_OK;
+    if (!dst || !src || !staging) return fail(GEMM_ERR_INVALID_ARG, "null pointer");
+    const char* s0 = static_cast<const char*>(src);
+    const char* g0 = static_cast<const char*>(staging);
+    const int64_t ring = chunk_bytes * nstage;
+    if (s0 < g0 + ring && g0 < s0 + bytes) return fail(GEMM_ERR_INVALID_ARG, "src and staging overlap");
+    // one event per slot: the DMA that last read the slot has finished when it completes
+    hipEvent_t ev[4];
+    int made = 0;
+    gemm_status_t result = GEMM_OK;
+    for (; made < nstage; ++made)
+        if (hipEventCreateWithFlags(&ev[made], hipEventDisableTiming) != hipSuccess) {
+            result = fail(GEMM_ERR_HIP, "hipEventCreateWithFlags failed");
+            break;
+        }
+    char* d0 = static_cast<char*>(dst);
+    char* slots = static_cast<char*>(staging);
+    const int64_t nchunks = result == GEMM_OK ? (bytes + chunk_bytes - 1) / chunk_bytes : 0;
+    for (int64_t c = 0; c < nchunks; ++c) {
+        const int slot = (int)(c % nstage);
+        const int64_t off = c * chunk_bytes;
+        const int64_t len = bytes - off < chunk_bytes ? bytes - off : chunk_bytes;
+        hipError_t e = hipSuccess;
+        if (c >= nstage) e = hipEventSynchronize(ev[slot]);  // wait until that slot's DMA has read it
+        if (e == hipSuccess) {
+            memcpy(slots + slot * chunk_bytes, s0 + off, (size_t)len);  // the CPU fills the slot ...
+            e = hipMemcpyAsync(d0 + off, slots + slot * chunk_bytes, (size_t)len, hipMemcpyHostToDevice, stream);
+        }
+        if (e == hipSuccess) e = hipEventRecord(ev[slot], stream);  // ... while the DMA drains the others
+        if (e != hipSuccess) { result = fail(GEMM_ERR_HIP, "staged copy failed: %s", hipGetErrorString(e)); break; }
+    }
+    // the staging buffer is the caller's again only once every DMA that reads it is done
+    for (int i = 0; i < made; ++i) {
+        if (result == GEMM_OK && i < nchunks) {
+            const hipError_t e = hipEventSynchronize(ev[i]);
+            if (e != hipSuccess) result = fail(GEMM_ERR_HIP, "staged copy failed: %s", hipGetErrorString(e));
+        }
+        (void)hipEventDestroy(ev[i]);
+    }
+    return result;
+}
+
 const char* gemm_status_string(gemm_status_t s) {
     switch (s) {
         case GEMM_OK: return "GEMM_OK";
