@@ -222,6 +222,56 @@ struct MfmaCompute {
             }
         }
     }
+    // Workgroup-wide epilogue through LDS for a 16-bit C with beta == 0 on a tile inside C
+    // whose rows start 16-byte aligned (every wave of the workgroup calls it; the ring's
+    // LDS is free once the K loop is done).  Each lane rounds alpha*acc and writes its
+    // quads into a BM x 256 tile in LDS -- row r, 16-byte chunk q at chunk position
+    // q ^ (r mod 32) of the row, so the 32 rows a write instruction touches spread over
+    // the banks -- then the workgroup stores whole 512-byte rows, 16 bytes per lane.  The
+    // lane layout of the accumulators would otherwise store 8-byte pieces of 32 rows per
+    // instruction.  Same values as epilogue(): RNE(alpha * acc).
+    template <int OUT, int NT>
+    __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m0, int n0) {
+        static_assert(OUT != DT_F32 && BN == 256 && MI == 32, "16-bit rows of 256 columns");
+        constexpr int RB = BN * 2;   // bytes per tile row
+        constexpr int CPR_C = RB / 16;
+        wait_lgkm0();
+        gemm::barrier();             // every wave's last fragment reads are done
+        const int w = wave_id();
+        const int wm = w / WN, wn = w % WN;
+        const int lane = lane_id();
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+            const int r = wm * WTM + i * MI + (lane % MI);
+#pragma unroll
+            for (int j = 0; j < TN; ++j)
+#pragma unroll
+                for (int g = 0; g < NR / 4; ++g) {
+                    const int c = wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
+                    uint16_t h[4];
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = p.alpha * acc[i][j][4 * g + e];
+                        h[e] = OUT == DT_BF16 ? f32_to_bf16_bits(v) : f32_to_f16_bits(v);
+                    }
+                    u32x2 pk;
+                    pk[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+                    pk[1] = (uint32_t)h[2] | ((uint32_t)h[3] << 16);
+                    const int off = r * RB + (((c >> 3) ^ (r & (CPR_C - 1))) << 4) + (c & 7) * 2;
+                    *reinterpret_cast<LDS_AS u32x2*>(smem + off) = pk;
+                }
+        }
+        wait_lgkm0();
+        gemm::barrier();
+        const int t = threadIdx.x;
+#pragma unroll
+        for (int k = 0; k < BM * CPR_C / NT; ++k) {
+            const int idx = t + NT * k;
+            const int r = idx / CPR_C, q = idx % CPR_C;
+            const u32x4 v = *reinterpret_cast<LDS_AS const u32x4*>(smem + r * RB + ((q ^ (r & (CPR_C - 1))) << 4));
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(p.C) + (int64_t)(m0 + r) * p.ldc + n0 + q * 8) = v;
+        }
+    }
 };
 
 // ---------------------------------------------------------------- direct ring kernel
@@ -389,17 +439,28 @@ void mfma_split_kernel(const GemmParams p) {
     const int m_keep = tm * BM, n_keep = tn * BN;
     const int m0 = min(m_keep, p.M - BM);
     const int n0 = min(n_keep, p.N - BN);
+    // 16-bit C, beta == 0, the tile inside C, rows 16-byte aligned: the C tile goes out
+    // through the (then idle) LDS ring as whole rows; the same test in every wave
+    constexpr bool LDS_EPI = OUT != DT_F32 && BN == 256 && S * STAGE >= BM * BN * 2;
+    const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
+                         n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
     if (wave_id() < NC) {
         SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
         gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        if constexpr (LDS_EPI) {
+            if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
+        }
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     } else {
         SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false> ops;
         ops.init((LDS_AS char*)(smem_raw));
         gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        if constexpr (LDS_EPI) {
+            if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
+        }
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     }
 }
