@@ -155,38 +155,44 @@ struct MfmaCompute {
         const int w = wave_id();
         const int wm = w / WN, wn = w % WN;
         const int lane = lane_id();
-        // Per block row i: with beta != 0, first the old C of all its TN*NR/4 quads (the
-        // loads then overlap), then the stores.  A tile inside C (not shifted, not cut) with
-        // vector-aligned rows takes unpredicated vectors (a wave-uniform choice): the
-        // per-element edge branches would otherwise make the compiler wait between quads.
+        // Per batch of quads (a block row's JB column blocks: all of them when that is at
+        // most 8 quads, else one, to bound the registers held): with beta != 0, first the
+        // old C of the batch (the loads then overlap), then the stores.  A tile inside C
+        // (not shifted, not cut) with vector-aligned rows takes unpredicated vectors (a
+        // wave-uniform choice): the per-element edge branches would otherwise make the
+        // compiler wait between quads.
+        constexpr int JB = TN * (NR / 4) <= 8 ? TN : 1;
         if (m0 == m_keep && n0 == n_keep && m0 + BM <= p.M && n0 + BN <= p.N && c_quads_aligned<OUT>(p)) {
 #pragma unroll
             for (int i = 0; i < TM; ++i) {
                 const int m = m0 + wm * WTM + i * MI + (lane % MI);
-                f32x4 old[TN][NR / 4];
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
+                for (int j0 = 0; j0 < TN; j0 += JB) {
+                    f32x4 old[JB][NR / 4];
 #pragma unroll
-                    for (int g = 0; g < NR / 4; ++g) old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-                if (p.beta != 0.0f) {  // one branch around the batch: its loads issue back to back
+                    for (int j = 0; j < JB; ++j)
 #pragma unroll
-                    for (int j = 0; j < TN; ++j)
+                        for (int g = 0; g < NR / 4; ++g) old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    if (p.beta != 0.0f) {  // one branch around the batch: its loads issue back to back
 #pragma unroll
-                        for (int g = 0; g < NR / 4; ++g)
-                            old[j][g] = load_c4_vec<OUT>(p, m, n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4);
-                }
+                        for (int j = 0; j < JB; ++j)
 #pragma unroll
-                for (int j = 0; j < TN; ++j)
-#pragma unroll
-                    for (int g = 0; g < NR / 4; ++g) {
-                        const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
-                        f32x4 v;
-                        v[0] = acc[i][j][4 * g + 0];
-                        v[1] = acc[i][j][4 * g + 1];
-                        v[2] = acc[i][j][4 * g + 2];
-                        v[3] = acc[i][j][4 * g + 3];
-                        store_c4_vec<OUT>(p, m, n, v, old[j][g]);
+                            for (int g = 0; g < NR / 4; ++g)
+                                old[j][g] = load_c4_vec<OUT>(p, m, n0 + wn * WTN + (j0 + j) * MI + g * 8 + (lane / MI) * 4);
                     }
+#pragma unroll
+                    for (int j = 0; j < JB; ++j)
+#pragma unroll
+                        for (int g = 0; g < NR / 4; ++g) {
+                            const int n = n0 + wn * WTN + (j0 + j) * MI + g * 8 + (lane / MI) * 4;
+                            f32x4 v;
+                            v[0] = acc[i][j0 + j][4 * g + 0];
+                            v[1] = acc[i][j0 + j][4 * g + 1];
+                            v[2] = acc[i][j0 + j][4 * g + 2];
+                            v[3] = acc[i][j0 + j][4 * g + 3];
+                            store_c4_vec<OUT>(p, m, n, v, old[j][g]);
+                        }
+                }
             }
             return;
         }
@@ -194,29 +200,32 @@ struct MfmaCompute {
         for (int i = 0; i < TM; ++i) {
             const int m = m0 + wm * WTM + i * MI + (lane % MI);
             const bool mok = m >= m_keep && m < p.M;
-            f32x4 old[TN][NR / 4];
 #pragma unroll
-            for (int j = 0; j < TN; ++j)
+            for (int j0 = 0; j0 < TN; j0 += JB) {
+                f32x4 old[JB][NR / 4];
 #pragma unroll
-                for (int g = 0; g < NR / 4; ++g) {
-                    // MI = 32: register group g covers n = 8g + 4*(lane/32) + 0..3;
-                    // MI = 16: the single group covers n = 4*(lane/16) + 0..3
-                    const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
-                    old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    if (p.beta != 0.0f && mok && n + 3 >= n_keep && n < p.N) old[j][g] = load_c4<OUT>(p, m, n, n_keep);
-                }
+                for (int j = 0; j < JB; ++j)
 #pragma unroll
-            for (int j = 0; j < TN; ++j) {
+                    for (int g = 0; g < NR / 4; ++g) {
+                        // MI = 32: register group g covers n = 8g + 4*(lane/32) + 0..3;
+                        // MI = 16: the single group covers n = 4*(lane/16) + 0..3
+                        const int n = n0 + wn * WTN + (j0 + j) * MI + g * 8 + (lane / MI) * 4;
+                        old[j][g] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        if (p.beta != 0.0f && mok && n + 3 >= n_keep && n < p.N) old[j][g] = load_c4<OUT>(p, m, n, n_keep);
+                    }
 #pragma unroll
-                for (int g = 0; g < NR / 4; ++g) {
-                    const int n = n0 + wn * WTN + j * MI + g * 8 + (lane / MI) * 4;
-                    if (mok && n + 3 >= n_keep && n < p.N) {
-                        f32x4 v;
-                        v[0] = acc[i][j][4 * g + 0];
-                        v[1] = acc[i][j][4 * g + 1];
-                        v[2] = acc[i][j][4 * g + 2];
-                        v[3] = acc[i][j][4 * g + 3];
-                        store_c4<OUT>(p, m, n, v, old[j][g], n_keep);
+                for (int j = 0; j < JB; ++j) {
+#pragma unroll
+                    for (int g = 0; g < NR / 4; ++g) {
+                        const int n = n0 + wn * WTN + (j0 + j) * MI + g * 8 + (lane / MI) * 4;
+                        if (mok && n + 3 >= n_keep && n < p.N) {
+                            f32x4 v;
+                            v[0] = acc[i][j0 + j][4 * g + 0];
+                            v[1] = acc[i][j0 + j][4 * g + 1];
+                            v[2] = acc[i][j0 + j][4 * g + 2];
+                            v[3] = acc[i][j0 + j][4 * g + 3];
+                            store_c4<OUT>(p, m, n, v, old[j][g], n_keep);
+                        }
                     }
                 }
             }
@@ -441,6 +450,8 @@ void mfma_split_kernel(const GemmParams p) {
     const int n0 = min(n_keep, p.N - BN);
     // 16-bit C, beta == 0, the tile inside C, rows 16-byte aligned: the C tile goes out
     // through the (then idle) LDS ring as whole rows; the same test in every wave
+    // (an fp32 C through LDS, in two passes of raw sums, measured 3% slower on the
+    // irregular-tail workload than the quad stores, so fp32 keeps those)
     constexpr bool LDS_EPI = OUT != DT_F32 && BN == 256 && S * STAGE >= BM * BN * 2;
     const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
                          n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
