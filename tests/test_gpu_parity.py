@@ -199,6 +199,7 @@ RING_STAGES = [
     ("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3, 4], 512, 384, 1024),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 5, [1, 2, 3, 4], 512, 384, 1024),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 4, [1, 2, 3, 4], 256, 320, 512),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 7, [1, 2, 3, 4], 96, 64, 320),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 3, [1, 2, 3, 4], 96, 64, 160),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, [1, 2, 3, 4], 512, 768, 640),
@@ -252,6 +253,7 @@ def test_xcd_order_does_not_change_results():
     (K_VALU_RING, 5, 3, 512, 256, 512, ROW, ROW),
     (K_VALU_RING, 4, 2, 256, 192, 256, ROW, ROW),
     (K_VALU_RING, 6, 4, 384, 128, 320, ROW, ROW),
+    (K_VALU_RING, 7, 2, 256, 256, 256, ROW, ROW),
     (K_VALU_RING, 2, 1, 192, 128, 64, ROW, ROW),
     (K_VALU_STAGED, 1, 2, 131, 77, 50, COL, COL),
     (K_VALU_STAGED, 3, 1, 45, 33, 19, ROW, COL),
@@ -452,12 +454,12 @@ def test_ring_tiles_on_ragged_edges(ts):
         assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
 
 
-@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2)])
+@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2), (7, 2)])
 def test_valu_ring_on_ragged_edges(tile, S):
     """fp32 direct ring with M and N not multiples of the tile (N a multiple of 4, so the
     shifted last column tile stays 16-byte aligned; row pitch padded): edge tiles shifted
     inward, every element stored once, exact."""
-    for (M, N, K, ldb) in ((300, 260, 48, 264), (130, 100, 32, 104)):
+    for (M, N, K, ldb) in ((300, 260, 64, 264), (130, 100, 32, 104)):
         say(f"[ragged valu] tile={tile} S={S} {M}x{N}x{K} ldb={ldb}")
         p = problem("f32", "f32", M, N, K, ROW, ROW, dist="int2", seed=101, ldb=ldb)
         got = run(p, kernel=K_VALU_RING, tile=tile, nstage=S)

@@ -45,6 +45,7 @@ const Tile kValuRing[] = {
     {4, 128, 64, 16, 128, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // tile 1 with 4-k steps
     {5, 128, 64, 16, 256, S1 | S2 | S3 | S4, 4, (128 * 16 + 16 * 64) * 4},  // 8x4 per thread
     {6, 128, 64, 16, 256, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // 4x8 per thread
+    {7, 32, 32, 32, 64, S1 | S2 | S3 | S4, 2, (32 * 32 + 32 * 32) * 4},     // tile 3, 32-deep slabs
 };
 // The fp32 ring tile used for problems of >= 512 128x64 tiles: 256 threads of 8x4, 4-k
 // steps, four slots (the fastest measured on fp32 4096^3 NN, 1-2% ahead of three).
@@ -228,8 +229,10 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     if (kernel == 0) {
         // Automatic: the direct ring when the operands allow it, else the staged loader.
         if (!mfma) {
+            // small problems: 32x32 tiles with 32-deep slabs (half the barriers of the
+            // 16-deep tile 3; fp32 256^3 11.9 vs 12.3 us)
             const Tile* big = find_tile(kValuRing, kValuRingDefault);
-            const Tile* small = find_tile(kValuRing, 3);
+            const Tile* small = find_tile(kValuRing, 7);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
             const Tile* pick = (opts.tile ? find_tile(kValuRing, opts.tile) : (many ? big : small));
             if (pick && ring_ok(q, *pick, false, &why)) { kernel = GEMM_KERNEL_VALU_RING; t = pick; }
