@@ -30,7 +30,9 @@
  *   nothing, keeps no pointer after returning and holds no mutable global state apart
  *   from a thread-local error string; calls are reentrant.  C must not overlap A or B
  *   (not checked).  Misaligned pointers or leading dimensions are never an error: they
- *   select a slower load path.
+ *   select a slower load path, or, given a caller-owned workspace (gemm_*_ws), a
+ *   one-pass rewrite of the operands for the fast path.  (gemm_h2d_staged alone takes
+ *   host memory.)
  *
  * Streams: the work is enqueued on `stream` (NULL = the null stream) and the call
  *   returns without synchronising.  Faults during execution surface at the caller's
