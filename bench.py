@@ -291,7 +291,8 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE={world}); "
-              "a GEMM shards into independent output tiles, see DESIGN.md", file=sys.stderr)
+              "a GEMM shards into independent output tiles, one GPU's share is this same kernel at a smaller M or N",
+              file=sys.stderr)
         sys.exit(2)
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
