@@ -9,8 +9,8 @@
 // runs on the copies.  Zero padding along K adds products 0*0 = +0 to every sum, so the
 // result is that of the unpadded problem.
 //
-// One launch handles up to two jobs (A and B).  Each workgroup owns a 64 x 64 tile of one
-// job's output.  Output row r, column c (c < len_pad, a multiple of 64):
+// One launch handles up to two jobs (A and B).  Each workgroup owns two consecutive 64 x 64
+// tiles of one job's output.  Output row r, column c (c < len_pad, a multiple of 64):
 //   trans = 0: src[r*ld + c]   (the source is already contiguous along K): rows are
 //              copied 16 bytes per lane, coalesced on both sides;
 //   trans = 1: src[c*ld + r]   (contiguous along the other index): the tile goes through
@@ -53,70 +53,102 @@ __device__ __forceinline__ u32x4 load8_partial(const uint16_t* src, int64_t idx,
     return t;
 }
 
-// Every lane issues all of its loads before its first store: the compiler cannot move
-// a load of src above a store to dst (they might alias), so interleaving them would
-// leave one load in flight per lane.
-__device__ __forceinline__ void pack_rows(const PackJob& j, int r0, int c0) {
+// A workgroup packs kTilesPerWg consecutive 64 x 64 tiles of one job.  Every lane issues
+// all of its loads (for all its tiles) before its first store: the compiler cannot move a
+// load of src above a store to dst (they might alias), so interleaving them would leave
+// one load in flight per lane.
+constexpr int kTilesPerWg = 2;
+
+__device__ __forceinline__ void tile_origin(const PackJob& j, int t, int& r0, int& c0) {
+    r0 = (t / j.tiles_c) * kPackTile;
+    c0 = (t % j.tiles_c) * kPackTile;
+}
+
+__device__ __forceinline__ void pack_rows(const PackJob& j, int t0, int ntiles) {
     const int t = threadIdx.x;
-    u32x4 v[2];
+    u32x4 v[kTilesPerWg][2];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int r = r0 + (t >> 3) + 32 * pass;
-        const int c = c0 + 8 * (t & 7);
-        const int64_t idx = (int64_t)r * j.ld + c;
-        if (r >= j.rows) v[pass] = u32x4{0u, 0u, 0u, 0u};
-        else if (c + 8 <= j.len) v[pass] = load8(j.src, idx);
-        else v[pass] = load8_partial(j.src, idx, 1, j.len - c);  // K tail (n <= 0: all zeros)
+    for (int u = 0; u < kTilesPerWg; ++u) {
+        int r0, c0;
+        tile_origin(j, t0 + u, r0, c0);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int r = r0 + (t >> 3) + 32 * pass;
+            const int c = c0 + 8 * (t & 7);
+            const int64_t idx = (int64_t)r * j.ld + c;
+            if (u >= ntiles || r >= j.rows) v[u][pass] = u32x4{0u, 0u, 0u, 0u};
+            else if (c + 8 <= j.len) v[u][pass] = load8(j.src, idx);
+            else v[u][pass] = load8_partial(j.src, idx, 1, j.len - c);  // K tail (n <= 0: all zeros)
+        }
     }
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int r = r0 + (t >> 3) + 32 * pass;
-        const int c = c0 + 8 * (t & 7);
-        if (r < j.rows) *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c) = v[pass];
+    for (int u = 0; u < kTilesPerWg; ++u) {
+        int r0, c0;
+        tile_origin(j, t0 + u, r0, c0);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int r = r0 + (t >> 3) + 32 * pass;
+            const int c = c0 + 8 * (t & 7);
+            if (u < ntiles && r < j.rows) *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c) = v[u][pass];
+        }
     }
 }
 
-__device__ __forceinline__ void pack_trans(const PackJob& j, int r0, int c0, uint16_t* tile) {
+__device__ __forceinline__ void pack_trans(const PackJob& j, int t0, int ntiles, uint16_t* tiles) {
     const int t = threadIdx.x;
     // Load: source line c (contiguous along r), 8 consecutive r per lane; then store the
-    // 8 values as one 16-byte LDS row chunk tile[c - c0][r - r0 ..].
-    u32x4 in[2];
+    // 8 values as one 16-byte LDS row chunk of the tile.
+    u32x4 in[kTilesPerWg][2];
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int c = c0 + (t >> 3) + 32 * pass, r = r0 + 8 * (t & 7);
-        const int64_t idx = (int64_t)c * j.ld + r;
-        if (c >= j.len) in[pass] = u32x4{0u, 0u, 0u, 0u};
-        else if (r + 8 <= j.rows) in[pass] = load8(j.src, idx);
-        else in[pass] = load8_partial(j.src, idx, 1, j.rows - r);
+    for (int u = 0; u < kTilesPerWg; ++u) {
+        int r0, c0;
+        tile_origin(j, t0 + u, r0, c0);
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass) {
+            const int c = c0 + (t >> 3) + 32 * pass, r = r0 + 8 * (t & 7);
+            const int64_t idx = (int64_t)c * j.ld + r;
+            if (u >= ntiles || c >= j.len) in[u][pass] = u32x4{0u, 0u, 0u, 0u};
+            else if (r + 8 <= j.rows) in[u][pass] = load8(j.src, idx);
+            else in[u][pass] = load8_partial(j.src, idx, 1, j.rows - r);
+        }
     }
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass)
-        *reinterpret_cast<u32x4*>(tile + tile_at((t >> 3) + 32 * pass, 8 * (t & 7))) = in[pass];
+    for (int u = 0; u < kTilesPerWg; ++u)
+#pragma unroll
+        for (int pass = 0; pass < 2; ++pass)
+            *reinterpret_cast<u32x4*>(tiles + u * kPackTile * kPackTile + tile_at((t >> 3) + 32 * pass, 8 * (t & 7))) =
+                in[u][pass];
     __syncthreads();
     // Store: output row r, 8 consecutive c per lane, gathered from 8 LDS rows.
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-        const int rl = (t >> 3) + 32 * pass;
-        const int cl = 8 * (t & 7);
-        const int r = r0 + rl;
-        if (r >= j.rows) continue;
-        u32x4 v = {0u, 0u, 0u, 0u};
+    for (int u = 0; u < kTilesPerWg; ++u) {
+        int r0, c0;
+        tile_origin(j, t0 + u, r0, c0);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v[e >> 1] |= (uint32_t)tile[tile_at(cl + e, rl)] << ((e & 1) * 16);
-        *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c0 + cl) = v;
+        for (int pass = 0; pass < 2; ++pass) {
+            const int rl = (t >> 3) + 32 * pass;
+            const int cl = 8 * (t & 7);
+            const int r = r0 + rl;
+            if (u >= ntiles || r >= j.rows) continue;
+            u32x4 v = {0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                v[e >> 1] |= (uint32_t)tiles[u * kPackTile * kPackTile + tile_at(cl + e, rl)] << ((e & 1) * 16);
+            *reinterpret_cast<u32x4*>(j.dst + (int64_t)r * j.len_pad + c0 + cl) = v;
+        }
     }
 }
 
 __global__ __launch_bounds__(kPackThreads) void pack_kernel(PackParams p) {
-    __shared__ __attribute__((aligned(16))) uint16_t tile[kPackTile * kPackTile];
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[kTilesPerWg * kPackTile * kPackTile];
     int b = blockIdx.x;
     const int which = b < p.job[0].blocks ? 0 : 1;
     if (which) b -= p.job[0].blocks;
     const PackJob& j = p.job[which];
-    const int r0 = (b / j.tiles_c) * kPackTile;
-    const int c0 = (b % j.tiles_c) * kPackTile;
-    if (j.trans) pack_trans(j, r0, c0, tile);
-    else pack_rows(j, r0, c0);
+    const int t0 = b * kTilesPerWg;
+    const int ntiles = min(kTilesPerWg, j.ntiles - t0);
+    if (j.trans) pack_trans(j, t0, ntiles, tiles);
+    else pack_rows(j, t0, ntiles);
 }
 
 }  // namespace
@@ -125,11 +157,13 @@ hipError_t launch_pack(PackParams p, hipStream_t st) {
     int64_t total = 0;
     for (int i = 0; i < 2; ++i) {
         PackJob& j = p.job[i];
-        if (j.rows <= 0) { j.blocks = 0; j.tiles_c = 1; continue; }
+        if (j.rows <= 0) { j.blocks = 0; j.ntiles = 0; j.tiles_c = 1; continue; }
         if (j.len_pad % kPackTile || j.len > j.len_pad) return hipErrorInvalidValue;
         j.tiles_c = j.len_pad / kPackTile;
-        const int64_t blocks = (int64_t)((j.rows + kPackTile - 1) / kPackTile) * j.tiles_c;
-        if (blocks > INT32_MAX) return hipErrorInvalidValue;
+        const int64_t ntiles = (int64_t)((j.rows + kPackTile - 1) / kPackTile) * j.tiles_c;
+        const int64_t blocks = (ntiles + kTilesPerWg - 1) / kTilesPerWg;
+        if (ntiles > INT32_MAX) return hipErrorInvalidValue;
+        j.ntiles = (int)ntiles;
         j.blocks = (int)blocks;
         total += blocks;
     }

@@ -31,15 +31,15 @@ hipError_t launch_pipe_copy(int nstage, const CopyParams& p, int64_t grid, hipSt
 // Operand repacking for the direct ring: dst is rows x len_pad 16-bit elements,
 // row-major, 16-byte aligned (len_pad a multiple of 64); dst[r][c] = src(r, c) for
 // c < len, +0 beyond, with src(r, c) = src[r*ld + c] (trans = 0) or src[c*ld + r]
-// (trans = 1).  A job with rows == 0 is skipped.  blocks / tiles_c are filled by the
-// launcher.
+// (trans = 1).  A job with rows == 0 is skipped.  tiles_c / ntiles / blocks are filled
+// by the launcher.
 constexpr int kPackThreads = 256;
 struct PackJob {
     const uint16_t* src;
     uint16_t* dst;
     int64_t ld;
     int rows, len, len_pad, trans;
-    int tiles_c, blocks;
+    int tiles_c, ntiles, blocks;
 };
 struct PackParams {
     PackJob job[2];

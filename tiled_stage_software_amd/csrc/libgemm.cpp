@@ -408,11 +408,11 @@ gemm_status_t run_ws(const Problem& q, const gemm_opts_t* opts, void* ws, size_t
     char* base = static_cast<char*>(ws);
     if (pp.a) {  // output row m, column k: A[m*lda + k] (row-major) or A[k*lda + m]
         pk.job[0] = {static_cast<const uint16_t*>(q.A), reinterpret_cast<uint16_t*>(base), q.lda, (int)q.M, (int)q.K,
-                     (int)pp.kp, q.la == GEMM_COL_MAJOR ? 1 : 0, 0, 0};
+                     (int)pp.kp, q.la == GEMM_COL_MAJOR ? 1 : 0, 0, 0, 0};
     }
     if (pp.b) {  // output row n, column k: B[n*ldb + k] (column-major) or B[k*ldb + n]
         pk.job[1] = {static_cast<const uint16_t*>(q.B), reinterpret_cast<uint16_t*>(base + pp.a_bytes), q.ldb,
-                     (int)q.N, (int)q.K, (int)pp.kp, q.lb == GEMM_ROW_MAJOR ? 1 : 0, 0, 0};
+                     (int)q.N, (int)q.K, (int)pp.kp, q.lb == GEMM_ROW_MAJOR ? 1 : 0, 0, 0, 0};
     }
     hipError_t e = gemm::launch_pack(pk, stream);
     if (e != hipSuccess) return fail(GEMM_ERR_HIP, "pack launch failed: %s", hipGetErrorString(e));
