@@ -46,6 +46,7 @@ const Tile kValuRing[] = {
     {5, 128, 64, 16, 256, S1 | S2 | S3 | S4, 4, (128 * 16 + 16 * 64) * 4},  // 8x4 per thread
     {6, 128, 64, 16, 256, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // 4x8 per thread
     {7, 32, 32, 32, 64, S1 | S2 | S3 | S4, 2, (32 * 32 + 32 * 32) * 4},     // tile 3, 32-deep slabs
+    {8, 128, 64, 32, 256, S1 | S2 | S3 | S4, 2, (128 * 32 + 32 * 64) * 4},  // tile 5, 32-deep slabs
 };
 // The fp32 ring tile used for problems of >= 512 128x64 tiles: 256 threads of 8x4, 4-k
 // steps, four slots (the fastest measured on fp32 4096^3 NN, 1-2% ahead of three).
