@@ -176,3 +176,21 @@ def test_rewritten_operands_bit_identical_across_stage_counts(tile, stages):
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
     assert err_vs_oracle(p, outs[0]) <= TOL["bf16"]
+
+
+def test_matmul_wrapper_with_an_automatic_workspace():
+    """libgemm.matmul(..., workspace="auto") on torch views: B given as a transposed
+    (N-contiguous) view, fp32 C with alpha / beta; exact on small integers."""
+    g = torch.Generator().manual_seed(17)
+    M, N, K = 300, 260, 130
+    A = torch.randint(-2, 3, (M, K), generator=g).to(torch.bfloat16)
+    Bt = torch.randint(-2, 3, (N, K), generator=g).to(torch.bfloat16)   # B = Bt.T is column-major
+    C0 = torch.randint(-4, 5, (M, N), generator=g).to(torch.float32)
+    want = 0.5 * (A.double() @ Bt.double().T) + 1.0 * C0.double()
+    for B in (Bt.to(DEV).T, Bt.T.contiguous().to(DEV)):                   # column- then row-major B
+        say(f"[matmul ws] B strides {tuple(B.stride())}")
+        C = C0.to(DEV)
+        out = lg.matmul(A.to(DEV), B, C=C, alpha=0.5, beta=1.0, workspace="auto")
+        torch.cuda.synchronize()
+        assert out.data_ptr() == C.data_ptr()
+        assert torch.equal(out.cpu().double(), want)
