@@ -167,6 +167,18 @@ def test_lds_budget():
     assert s == lg.GEMM_ERR_UNSUPPORTED
 
 
+def test_split_tiles_keep_lds_for_the_c_tile():
+    # a 16-bit C of 256 columns is staged through LDS after the K loop: the one-slot ring of
+    # the 256x256 split tile still allocates the 128 KiB C tile; an fp32 C does not
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=24, nstage=1)
+    assert s == 0 and p.lds_bytes == 256 * 256 * 2
+    s, p = plan(BF16, F32, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=24, nstage=1)
+    assert s == 0 and p.lds_bytes == (256 + 256) * 64 * 2
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=24, nstage=1,
+                flags=lg.GEMM_FLAG_EQUAL_LDS)
+    assert s == 0 and p.lds_bytes == 2 * (256 + 256) * 64 * 2   # the 2-slot ring: no padding needed
+
+
 def test_forced_kernels_and_stages():
     for S in (1, 2, 3, 4):
         s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, kernel=lg.GEMM_KERNEL_VALU_RING, nstage=S)

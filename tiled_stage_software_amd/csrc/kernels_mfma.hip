@@ -442,7 +442,11 @@ template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, in
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_split_kernel(const GemmParams p) {
     static constexpr int STAGE = (BM + BN) * BK * 2;
-    __shared__ __attribute__((aligned(1024))) char smem_raw[S * STAGE];
+    // a 16-bit C tile of 256 columns leaves through LDS after the K loop (epilogue_lds):
+    // at least that much LDS whatever the ring (one workgroup per CU either way)
+    static constexpr int EPI = (OUT != DT_F32 && BN == 256) ? BM * BN * 2 : 0;
+    static constexpr int SMEM = S * STAGE > EPI ? S * STAGE : EPI;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
     int tm, tn;
     tile_coords(p, tm, tn);
     const int m_keep = tm * BM, n_keep = tn * BN;
@@ -452,7 +456,7 @@ void mfma_split_kernel(const GemmParams p) {
     // through the (then idle) LDS ring as whole rows; the same test in every wave
     // (an fp32 C through LDS, in two passes of raw sums, measured 3% slower on the
     // irregular-tail workload than the quad stores, so fp32 keeps those)
-    constexpr bool LDS_EPI = OUT != DT_F32 && BN == 256 && S * STAGE >= BM * BN * 2;
+    constexpr bool LDS_EPI = EPI > 0;
     const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
                          n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
     if (wave_id() < NC) {

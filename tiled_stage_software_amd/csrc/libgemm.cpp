@@ -148,6 +148,17 @@ gemm_status_t validate(const Problem& q) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// LDS a kernel of this tile allocates statically: the ring, or for the split-copy tiles
+// with 256 columns and a 16-bit C, at least the C tile (bm x 256 x 2 bytes), which their
+// epilogue stages through LDS after the K loop whatever the stage count.
+int static_lds(const Tile& t, int S, int kernel, int c_type) {
+    int lds = S * t.stage_bytes;
+    const bool split = t.id == 21 || t.id == 23 || t.id == 24 || t.id == 25 || t.id == 27 || t.id == 29;
+    if (kernel == GEMM_KERNEL_MFMA_RING && split && c_type != gemm::DT_F32 && t.bn == 256 && lds < t.bm * t.bn * 2)
+        lds = t.bm * t.bn * 2;
+    return lds;
+}
+
 // Can the direct global->LDS ring run this problem with this tile?
 bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
     const int es = elem_size(q.in_type);
@@ -285,7 +296,8 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     int S = opts.nstage ? opts.nstage : t->def_stage;
     if (!(t->stages & (1 << S)))
         return fail(GEMM_ERR_UNSUPPORTED, "nstage %d not built for tile %d of kernel %d", S, t->id, kernel);
-    if (S * t->stage_bytes > kLdsLimit)
+    const int lds = static_lds(*t, S, kernel, q.c_type);
+    if (lds > kLdsLimit)
         return fail(GEMM_ERR_UNSUPPORTED, "ring of %d x %d bytes exceeds the %d bytes of LDS", S, t->stage_bytes, kLdsLimit);
 
     plan->kernel = kernel;
@@ -293,12 +305,12 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     plan->tile = t->id;
     plan->bm = t->bm; plan->bn = t->bn; plan->bk = t->bk;
     plan->threads = t->threads;
-    plan->lds_bytes = S * t->stage_bytes;
+    plan->lds_bytes = lds;
     if (opts.flags & GEMM_FLAG_EQUAL_LDS) {
         int deepest = S;
         for (int d = GEMM_MAX_NSTAGE; d > S; --d)
-            if ((t->stages & (1 << d)) && d * t->stage_bytes <= kLdsLimit) { deepest = d; break; }
-        gp->lds_pad = (deepest - S) * t->stage_bytes;
+            if ((t->stages & (1 << d)) && static_lds(*t, d, kernel, q.c_type) <= kLdsLimit) { deepest = d; break; }
+        gp->lds_pad = static_lds(*t, deepest, kernel, q.c_type) - lds;
         plan->lds_bytes += gp->lds_pad;
     }
     gp->tiles_m = (int)cdiv(q.M, t->bm);
