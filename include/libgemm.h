@@ -28,7 +28,9 @@
  *
  * Pointers: A, B and C are DEVICE pointers owned by the caller.  The library allocates
  *   nothing, keeps no pointer after returning and holds no mutable global state apart
- *   from a thread-local error string; calls are reentrant.  C must not overlap A or B
+ *   from a thread-local error string and a per-device cache of the compute-unit count
+ *   (atomic: first calls from several threads at once are safe); calls are reentrant
+ *   and may come from any number of host threads.  C must not overlap A or B
  *   (not checked).  Misaligned pointers or leading dimensions are never an error: they
  *   select a slower load path, or, given a caller-owned workspace (gemm_*_ws), a
  *   one-pass rewrite of the operands for the fast path.  (gemm_h2d_staged alone takes
@@ -82,7 +84,7 @@ typedef enum gemm_kernel {
     GEMM_KERNEL_SCALE = 5        /* C = beta*C only (K == 0 or alpha == 0) */
 } gemm_kernel_t;
 
-#define GEMM_MAX_NSTAGE 5
+#define GEMM_MAX_NSTAGE 4
 
 /* Optional knobs for tests and benchmarks.  All-zero = library default. */
 typedef struct gemm_opts {
@@ -91,10 +93,11 @@ typedef struct gemm_opts {
                    n = n-1 slabs in flight while one is computed. Staged kernels: 1 or 2. */
     int kernel; /* gemm_kernel_t; 0 = automatic choice */
     int tile;   /* 0 = default tile of the kernel family, else a tile id (gemm_plan_t.tile) */
-    int flags;  /* bit 0: disable the XCD-aware workgroup order (plain row-major tile order);
-                   other bits must be 0 */
+    int flags;  /* GEMM_FLAG_* bits below; other bits must be 0 */
 } gemm_opts_t;
 
+/* Plain row-major tile order instead of the grouped, XCD-aware workgroup order (results
+ * are unchanged: every output tile is computed the same way wherever it runs). */
 #define GEMM_FLAG_NO_XCD_REMAP 1
 /* Allocate, whatever the stage count, the LDS of the deepest ring the tile offers, so that
  * nStage variants run at the same occupancy (the fair comparison: at natural occupancy a
@@ -110,7 +113,7 @@ typedef struct gemm_plan {
     int threads;       /* threads per workgroup */
     int lds_bytes;     /* LDS per workgroup */
     int64_t grid;      /* workgroups launched (0 if nothing is launched); for the persistent
-                          MFMA ring tiles (19, 20, 28) the number of output tiles, which one
+                          MFMA ring tiles (19, 28) the number of output tiles, which one
                           workgroup per compute unit walks */
     int packed;        /* gemm_workspace_size only: bit 0 / bit 1 = A / B is first rewritten
                           into the workspace (then the fields above describe the multiply of
@@ -227,7 +230,9 @@ gemm_status_t gemm_tune_ws(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layou
                            void* workspace, size_t workspace_bytes, int reps, gemm_opts_t* best, float* best_ms);
 
 /* The K-loop protocol of a kernel family, as the event list its mainloop executes
- * (host only, for checking the pipeline on the CPU).  Each event is 4 ints
+ * (host only, for checking the pipeline on the CPU).  nstage: 1..5 for the ring
+ * families (the protocol itself; kernels are built up to GEMM_MAX_NSTAGE), 1..2 for the
+ * staged ones.  Each event is 4 ints
  * {type, slab, slot, arg}:
  *   1 ISSUE    slab -> slot: asynchronous global->LDS copy of K-slab `slab` into ring
  *              slot `slot` (staged kernels: slot == -1, a global->register load);

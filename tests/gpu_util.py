@@ -136,3 +136,33 @@ def expected_rounded(exact: np.ndarray, out: str) -> np.ndarray:
     oracle defines it."""
     fmt = {"f32": oracle.FMT_F32, "bf16": oracle.FMT_BF16, "f16": oracle.FMT_F16}[out]
     return oracle.round_to(exact, fmt)
+
+
+def widened(p: inputs.Problem):
+    """The operands' storage widened (exactly) to fp64 once, for repeated oracle calls."""
+    a = p.A.storage.double().numpy()
+    b = p.B.storage.double().numpy()
+    c = None if p.C0 is None else p.C0.storage.double().numpy()
+    return a, b, c
+
+
+def whole_matrix(p: inputs.Problem, C: torch.Tensor, exact: bool = False, batch: int = 512) -> float:
+    """Every element of the device result C (M x N, CPU) against the oracle, computed in
+    batches of rows so that host memory stays bounded.  exact=False: the normalised error
+    ||C - Cref||_inf / (K max|A| max|B|) over the whole matrix, raw (the output rounding
+    included).  exact=True: the number of elements that differ from the exact result
+    rounded (RNE) to the output type."""
+    a, b, c = widened(p)
+    la, lb = p.A.layout == inputs.COL, p.B.layout == inputs.COL
+    amax, bmax = max_abs(p.A), max_abs(p.B)
+    worst, bad = 0.0, 0
+    for r0 in range(0, p.M, batch):
+        rows = list(range(r0, min(p.M, r0 + batch)))
+        ref = oracle.gemm_f64(la, lb, p.M, p.N, p.K, p.alpha, a, p.A.ld, b, p.B.ld, p.beta, c,
+                              0 if p.C0 is None else p.C0.ld, rows=rows)
+        got = C[r0:r0 + len(rows)].double().numpy()
+        if exact:
+            bad += int(np.count_nonzero(got != expected_rounded(ref, p.out)))
+        else:
+            worst = max(worst, oracle.normalized_error(got, ref, p.K, amax, bmax))
+    return float(bad) if exact else worst

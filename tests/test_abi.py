@@ -329,3 +329,53 @@ def test_h2d_staged_rejects_bad_arguments_before_copying():
                        ((A16, H, 8192, H + 4096, 4096, 2), lg.GEMM_ERR_INVALID_ARG)):  # src overlaps the ring
         assert lg.gemm_h2d_staged(*args) == want, args
     assert lg.gemm_h2d_staged(A16, H, 0, H + (1 << 20), 4096, 2) == lg.GEMM_OK   # nothing to copy
+
+
+# --------------------------------------------------------------- failure paths without a GPU
+
+def _no_gpu_here():
+    import torch
+    return torch.cuda.device_count() == 0   # counts devices without initialising HIP
+
+
+@pytest.mark.skipif(not _no_gpu_here(), reason="needs a host without a GPU: the calls below pass fake device "
+                                                "addresses that a real launch would dereference")
+def test_launch_without_a_device_reports_hip_error():
+    """With no GPU present the HIP runtime refuses every launch: each entry point returns
+    GEMM_ERR_HIP with the runtime's message, after its own argument checks passed."""
+    cases = [
+        ("gemm_f32", lambda: lg.gemm_f32(ROW, ROW, 256, 256, 256, 1.0, A16, 256, B16, 256, 0.0, C16, 256)),
+        ("gemm_bf16 ring", lambda: lg.gemm_bf16(ROW, COL, 512, 512, 512, 1.0, A16, 512, B16, 512, 0.0, C16,
+                                                 lg.GEMM_BF16, 512)),
+        ("gemm_f16 staged", lambda: lg.gemm_f16(COL, ROW, 100, 70, 33, 1.0, A16, 100, B16, 70, 0.5, C16,
+                                                 lg.GEMM_F32, 70)),
+        ("scale", lambda: lg.gemm_bf16(ROW, COL, 64, 64, 0, 1.0, A16, 1, B16, 1, 0.5, C16, lg.GEMM_F32, 64)),
+        ("gemm_bf16_ws pack", lambda: lg.gemm_bf16_ws(ROW, ROW, 4000, 3000, 2049, 0.5, A16, 2049, B16, 3000, 1.0,
+                                                     C16, lg.GEMM_F32, 3000, 0, None, 0x40000000, 1 << 26)),
+        ("gemm_pipe_copy", lambda: lg.gemm_pipe_copy(A16, 0x800000, 1 << 16, 2)),
+    ]
+    for name, call in cases:
+        s = call()
+        msg = lg.gemm_last_error()
+        assert s == lg.GEMM_ERR_HIP, (name, s, msg)
+        assert msg and ("fail" in msg or "error" in msg.lower()), (name, msg)
+    # the tuner's event creation or first launch fails the same way, before any timing
+    best, ms = lg.GemmOpts(), ctypes.c_float(0)
+    s = lg.load().gemm_tune(BF16, BF16, ROW, COL, 512, 512, 512, 1.0, A16, 512, B16, 512, 0.0, C16, 512, None, 2,
+                            ctypes.byref(best), ctypes.byref(ms))
+    assert s == lg.GEMM_ERR_HIP and lg.gemm_last_error()
+    # a later call's own argument error still wins over the missing device
+    assert lg.gemm_f32(ROW, ROW, -1, 1, 1, 1.0, A16, 1, B16, 1, 0.0, C16, 1) == lg.GEMM_ERR_INVALID_ARG
+
+
+def test_matmul_rejects_overlapping_c_before_any_launch():
+    """An expanded (stride 0) or row-overlapping C view would make the kernels write past
+    its storage: the binding refuses it before calling the library."""
+    import torch
+    A = torch.zeros(4, 8, dtype=torch.bfloat16)
+    B = torch.zeros(8, 8, dtype=torch.bfloat16)
+    for C in (torch.empty(1, 8).expand(4, 8), torch.empty(40).as_strided((4, 8), (4, 1)),
+              torch.empty(1, 1).expand(4, 1)):
+        Bv = B if C.shape[1] == 8 else B[:, :1]
+        with pytest.raises(ValueError, match="overlap"):
+            lg.matmul(A, Bv, C=C)

@@ -12,7 +12,7 @@ import pytest
 import torch
 
 from gpu_util import (DEV, TOL, say, gpu_gemm, c_logical, oracle_ref, err_vs_oracle, sample_rows,
-                      expected_rounded, max_abs)
+                      expected_rounded, max_abs, whole_matrix)
 from oracle import oracle
 from tiled_stage_software_amd import inputs, libgemm as lg
 
@@ -63,9 +63,10 @@ FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= 
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, 2, 512, 512, 256),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 3, 2, 256, 384, 128),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, 4, 256, 512, 256),
-    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 7, 2, 512, 256, 256),
-    ("f16", "f32", ROW, COL, K_MFMA_RING, 8, 2, 256, 512, 256),
-    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, 4, 256, 256, 256),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, 2, 512, 256, 256),
+    ("f16", "f32", ROW, COL, K_MFMA_RING, 26, 2, 256, 512, 256),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 25, 4, 256, 256, 256),
+    ("f16", "f16", ROW, COL, K_MFMA_RING, 29, 1, 384, 256, 256),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, 2, 200, 136, 77),
     ("f16", "f16", COL, ROW, K_MFMA_STAGED, 1, 1, 129, 257, 40),
 ]
@@ -164,33 +165,58 @@ def test_workload_small_vs_oracle(name):
     assert err <= TOL[cfg["dtype"]]
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
-def test_workload_full_size_sampled(name):
-    """Full configuration sizes in the launch configuration the benchmark times; the
-    oracle checks a row sample that touches every 256-row block and every column."""
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+def test_workload_full_size_whole_matrix(name):
+    """Full configuration sizes in the launch configuration the benchmark times: every
+    element against the oracle, the stated bar unadjusted (output rounding included).
+    (The irregular-tail workload runs through the workspace entry point, as the benchmark
+    launches it: tests/test_gpu_workspace.py.)"""
     cfg = inputs.CONFIGS[name]
     p = inputs.make_problem(cfg)
     s, plan = lg.gemm_plan({"f32": 0, "bf16": 1, "f16": 2}[p.dtype], {"f32": 0, "bf16": 1, "f16": 2}[p.out],
                            p.A.layout, p.B.layout, p.M, p.N, p.K, p.alpha, 16, p.A.ld, 16, p.B.ld, p.beta, 16, p.N)
     say(f"[{name} full] M={p.M} N={p.N} K={p.K} plan={plan.as_dict()}")
     got = run(p)
-    rows = sample_rows(p.M)
-    err = err_vs_oracle(p, got, rows, raw=True)   # the stated bar, output rounding included
-    say(f"  rows={len(rows)} err={err:.3e}")
-    assert err <= TOL[cfg["dtype"]]
     assert not torch.isnan(got).any()
+    err = whole_matrix(p, got)
+    say(f"  all {p.M} rows: err={err:.3e}")
+    assert err <= TOL[cfg["dtype"]]
 
 
 @pytest.mark.parametrize("name", ["c3", "c4"])
 def test_full_size_small_integers_bit_exact(name):
-    """Whole-matrix bit-exactness at the full MFMA shapes with integer inputs."""
+    """Whole-matrix bit-exactness at the full MFMA shapes with integer inputs (every sum
+    exact in fp32): every element equals the exact result rounded to the output type."""
     cfg = inputs.CONFIGS[name]
     p = inputs.make_problem(cfg, dist="int2")
     say(f"[{name} full int2]")
     got = run(p)
-    rows = sample_rows(p.M)
-    exact = oracle_ref(p, rows)
-    assert np.array_equal(got[rows].double().numpy(), expected_rounded(exact, p.out))
+    bad = whole_matrix(p, got, exact=True)
+    say(f"  all {p.M} rows: {int(bad)} elements differ")
+    assert bad == 0
+
+
+FULL_STAGES = [  # (workload, kernel family, tile, stage counts): the default tiles at full size
+    ("c2", K_VALU_RING, 5, [1, 2, 3, 4]),
+    ("c3", K_MFMA_RING, 24, [1, 2]),
+    ("c4", K_MFMA_RING, 24, [1, 2]),
+]
+
+
+@pytest.mark.parametrize("case", FULL_STAGES, ids=lambda c: c[0])
+def test_full_shape_bit_identical_across_stage_counts(case):
+    """At the full configuration shapes: the ring depth changes no bit of the output (every
+    accumulator sees the same k order), and a repeated run changes none either."""
+    name, kern, tile, stages = case
+    p = inputs.make_problem(inputs.CONFIGS[name])
+    outs = []
+    for S in stages:
+        say(f"[{name} full stages] tile={tile} nstage={S}")
+        outs.append(run(p, kernel=kern, tile=tile, nstage=S))
+    outs.append(run(p, kernel=kern, tile=tile, nstage=stages[-1]))
+    bits = torch.int32 if outs[0].dtype == torch.float32 else torch.int16
+    for o in outs[1:]:
+        assert torch.equal(o.view(bits), outs[0].view(bits))
 
 
 # --------------------------------------------------------------- stage counts
@@ -204,15 +230,14 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, [1, 2], 768, 512, 512),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, [1, 2, 3, 4], 512, 768, 640),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 3, [1, 2, 3, 4], 384, 256, 704),
-    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 9, [3, 4], 512, 768, 640),
-    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 13, [1, 2], 768, 512, 512),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 25, [3, 4], 512, 768, 640),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, [1, 2], 768, 512, 576),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 29, [1, 2], 600, 768, 448),
-    ("f16", "f16", ROW, COL, K_MFMA_RING, 21, [1, 2], 512, 768, 448),
+    ("f16", "f16", ROW, COL, K_MFMA_RING, 23, [1, 2], 512, 768, 448),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 26, [1, 2], 768, 600, 576),
-    ("bf16", "f32", ROW, COL, K_MFMA_RING, 27, [1, 2], 600, 768, 448),
+    ("bf16", "f32", ROW, COL, K_MFMA_RING, 29, [1, 2], 600, 768, 448),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 19, [2, 3], 2304, 4352, 320),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
@@ -268,14 +293,20 @@ def test_fp32_matches_fma_chain_bit_for_bit(kern, tile, S, M, N, K, la, lb):
         assert np.array_equal(got.numpy(), want), np.argwhere(got.numpy() != want)[:5]
 
 
-def test_fp32_4096_sampled_rows_fma_chain():
+def test_fp32_4096_whole_matrix_fma_chain():
+    """fp32 4096^3 at full size: every element equal, bit for bit, to one fmaf chain per
+    output in ascending k."""
     p = inputs.make_problem(inputs.CONFIGS["c2"])
     say("[fma chain c2 full]")
-    got = run(p)
-    rows = sample_rows(p.M)[:12]
-    want = oracle.sgemm_fma_chain(False, False, p.M, p.N, p.K, 1.0, p.A.storage, p.A.ld, p.B.storage, p.B.ld,
-                                  rows=rows)
-    assert np.array_equal(got[rows].numpy(), want)
+    got = run(p).numpy()
+    bad = 0
+    for r0 in range(0, p.M, 512):
+        rows = list(range(r0, min(p.M, r0 + 512)))
+        want = oracle.sgemm_fma_chain(False, False, p.M, p.N, p.K, 1.0, p.A.storage, p.A.ld, p.B.storage, p.B.ld,
+                                      rows=rows)
+        bad += int(np.count_nonzero(got[r0:r0 + len(rows)] != want))
+    say(f"  all {p.M} rows: {bad} elements differ")
+    assert bad == 0
 
 
 # --------------------------------------------------------------- edge sweep
@@ -399,7 +430,7 @@ def test_every_planned_variant_launches_and_matches(v):
 
 # --------------------------------------------------------------- persistent tiles
 
-PERSISTENT = [(19, 2), (19, 3), (20, 3), (28, 2)]
+PERSISTENT = [(19, 2), (19, 3), (28, 2)]
 
 
 @pytest.mark.parametrize("shape", [(4096, 4096, 192), (4100, 3000, 320), (2048, 2560, 128), (8192, 4352, 128)],
@@ -439,7 +470,7 @@ def test_equal_lds_padding_changes_no_bit(case):
         assert torch.equal(a, b)
 
 
-RAGGED_TILES = [(23, 2), (24, 2), (24, 1), (21, 2), (18, 3), (17, 1), (22, 3), (13, 2), (26, 2), (27, 1), (29, 2)]
+RAGGED_TILES = [(23, 2), (24, 2), (24, 1), (18, 3), (18, 1), (25, 3), (26, 2), (26, 1), (29, 1), (29, 2), (1, 2), (2, 4)]
 
 
 @pytest.mark.parametrize("ts", RAGGED_TILES, ids=lambda t: f"t{t[0]}-s{t[1]}")

@@ -45,10 +45,16 @@ def _compile(src: str, extra) -> str:
 
 
 def build(extra=(), jobs: int = 8, verbose: bool = True) -> str:
-    """Compile every HIP source and link libgemm.so (always rebuilds)."""
+    """Compile every HIP source and link libgemm.so (always rebuilds).  With the
+    environment variable GEMM_ALL_TILES=1 the matrix-core variants that lose on every
+    measured workload are built too (they are left out of the default library)."""
+    extra = list(extra)
+    if os.environ.get("GEMM_ALL_TILES", "0") not in ("", "0"):
+        extra.append("-DGEMM_ALL_TILES")
     os.makedirs(BUILD, exist_ok=True)
     os.makedirs(os.path.dirname(LIB), exist_ok=True)
-    srcs = sources()
+    # the matrix-core units take longest: start them first
+    srcs = sorted(sources(), key=lambda f: (not os.path.basename(f).startswith("kernels_mfma_"), f))
     with cf.ThreadPoolExecutor(max_workers=max(1, min(jobs, len(srcs)))) as ex:
         objs = list(ex.map(lambda s: _compile(s, list(extra)), srcs))
     tmp = LIB + ".tmp%d" % os.getpid()

@@ -1,0 +1,8 @@
+// kernels_mfma_f16_f16.hip -- the matrix-core kernels for f16 inputs and a f16 C
+// (explicit instantiation of the launch tables in mfma.hpp).
+#include "mfma.hpp"
+
+namespace gemm {
+template hipError_t ring_dispatch<_Float16, DT_F16>(int tile, int S, const GemmParams& p, hipStream_t st);
+template hipError_t staged_dispatch<_Float16, DT_F16>(int tile, int S, const GemmParams& p, hipStream_t st);
+}  // namespace gemm

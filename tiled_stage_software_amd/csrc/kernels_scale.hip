@@ -1,5 +1,7 @@
 // kernels_scale.hip -- C = beta*C, the BLAS quick return when K == 0 or alpha == 0
 // (beta == 0 writes zeros without reading C).
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -35,15 +37,17 @@ hipError_t launch_scale(const GemmParams& p, hipStream_t st) {
 }
 
 int num_compute_units() {
-    static int cache[64] = {0};
+    // One atomic per device, so that first calls from several host threads do not race:
+    // each may query, and all store the same value.
+    static std::atomic<int> cache[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cache[dev] == 0) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (n <= 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);
     }
-    return cache[dev];
+    return n;
 }
 
 }  // namespace gemm

@@ -13,7 +13,9 @@ hipError_t launch_mfma_ring(int in_type, int tile, int nstage, const GemmParams&
 hipError_t launch_mfma_staged(int in_type, int tile, int nstage, const GemmParams& p, hipStream_t st);
 hipError_t launch_scale(const GemmParams& p, hipStream_t st);
 
-// Compute units of the current device (cached per device; 256 if the query fails).
+// Compute units of the current device (cached per device in an atomic, so concurrent
+// first calls are safe; 256 when no device can be queried, e.g. planning on a host
+// without a GPU).
 int num_compute_units();
 
 // Pipelined streaming copy (the bandwidth-bound control): `slabs` slabs of kCopySlab

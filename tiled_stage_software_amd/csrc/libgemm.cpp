@@ -59,6 +59,15 @@ const Tile kMfmaRing[] = {
     {1, 256, 256, 64, 256, S1 | S2, 2, (256 + 256) * 64 * 2},
     {2, 256, 256, 32, 256, S1 | S2 | S3 | S4, 3, (256 + 256) * 32 * 2},
     {3, 128, 128, 64, 256, S1 | S2 | S3 | S4, 2, (128 + 128) * 64 * 2},
+    {18, 256, 128, 64, 384, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 2 producer waves
+    {19, 256, 128, 64, 384, S2 | S3, 3, (256 + 128) * 64 * 2},    // tile 18, persistent
+    {23, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // 8 waves (2x4 of 128x64), copies by one wave per SIMD
+    {24, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 23, copies spread
+    {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
+    {26, 256, 192, 64, 512, S1 | S2, 2, (256 + 192) * 64 * 2},    // tile 23's scheme, 4x2 waves of 64x96
+    {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
+    {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64, copies spread
+#ifdef GEMM_ALL_TILES  // variants that lose on every workload measured (built on request)
     {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies spread over the slab
     {5, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},     // copies spread
     {6, 128, 128, 64, 256, S2 | S3, 2, (128 + 128) * 64 * 2},     // copies spread
@@ -73,18 +82,11 @@ const Tile kMfmaRing[] = {
     {15, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 5, pinned
     {16, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 9, pinned
     {17, 256, 128, 64, 512, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 4 producer waves
-    {18, 256, 128, 64, 384, S1 | S2 | S3, 3, (256 + 128) * 64 * 2},  // 4 consumer + 2 producer waves
-    {19, 256, 128, 64, 384, S2 | S3, 3, (256 + 128) * 64 * 2},    // tile 18, persistent
     {20, 256, 128, 64, 512, S3, 3, (256 + 128) * 64 * 2},         // tile 17, persistent
     {22, 256, 128, 64, 320, S3, 3, (256 + 128) * 64 * 2},         // 4 consumer + 1 producer wave
     {21, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // 8 waves, copies by 4 of them
-    {23, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // same, 2x4 waves
-    {24, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 23, copies spread
-    {25, 256, 256, 32, 512, S3 | S4, 3, (256 + 256) * 32 * 2},    // tile 23 with BK 32, spread
-    {26, 256, 192, 64, 512, S1 | S2, 2, (256 + 192) * 64 * 2},    // tile 23's scheme, 4x2 waves of 64x96
     {27, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64
-    {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
-    {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 27, copies spread
+#endif
 };
 // The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles (and
 // the cost model below keeps 256x256): 256x256x64, two slots, eight waves (2x4 of
@@ -99,7 +101,6 @@ const Tile kMfmaStaged[] = {
 };
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
-constexpr int64_t kComputeUnits = 256;  // compute units of the MI355X (planning is host-only)
 
 template <size_t N>
 const Tile* find_tile(const Tile (&t)[N], int id) {
@@ -262,12 +263,15 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
             if (many) {
                 // One workgroup of these tiles is resident per compute unit, so the grid
                 // runs in ceil(tiles / CUs) rounds of one tile each: take the shape with
-                // the least work per CU, ceil(tiles / CUs) * bm * bn.  Ties keep the
-                // earlier shape (256x256 first; 192x256 measured faster than 256x192).
+                // the least work per CU, ceil(tiles / CUs) * bm * bn, on the compute units
+                // of the current device (the same count the persistent launchers use).
+                // Ties keep the earlier shape (256x256 first; 192x256 measured faster
+                // than 256x192).
+                const int64_t cus = gemm::num_compute_units();
                 int64_t best = -1;
                 for (int id : {kMfmaRingDefault, 29, 26}) {
                     const Tile* c = find_tile(kMfmaRing, id);
-                    const int64_t cost = cdiv(cdiv(q.M, c->bm) * cdiv(q.N, c->bn), kComputeUnits) * c->bm * c->bn;
+                    const int64_t cost = cdiv(cdiv(q.M, c->bm) * cdiv(q.N, c->bn), cus) * c->bm * c->bn;
                     if (best < 0 || cost < best) { best = cost; big = c; }
                 }
             }

@@ -26,7 +26,7 @@ GEMM_F32, GEMM_BF16, GEMM_F16 = 0, 1, 2
  GEMM_KERNEL_MFMA_STAGED, GEMM_KERNEL_SCALE) = range(6)
 GEMM_FLAG_NO_XCD_REMAP = 1
 GEMM_FLAG_EQUAL_LDS = 2
-GEMM_MAX_NSTAGE = 5
+GEMM_MAX_NSTAGE = 4
 
 KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: "mfma_staged", 5: "scale"}
 
@@ -278,7 +278,10 @@ def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, 
         C = torch.empty((M, N), dtype=out_dtype, device=A.device)
     if C.dim() != 2 or tuple(C.shape) != (M, N) or (N > 1 and C.stride(1) != 1):
         raise ValueError("C must be an M x N row-major view")
-    ldc = max(C.stride(0), N) if M > 1 else max(N, 1)
+    if M > 1 and C.stride(0) < N:
+        # an expanded or row-overlapping view: the kernels would write past its storage
+        raise ValueError(f"C rows overlap (stride {C.stride(0)} < N = {N})")
+    ldc = C.stride(0) if M > 1 else max(N, 1)
     st = stream if stream is not None else torch.cuda.current_stream(A.device).cuda_stream
     o = _opts(nstage, kernel, tile, flags)
     if A.dtype == torch.float32:
@@ -301,6 +304,11 @@ def matmul(A, B, C=None, alpha: float = 1.0, beta: float = 0.0, out_dtype=None, 
                                                    B.data_ptr(), lb[1], beta, C.data_ptr(), ldc, o)
                 check(s)
                 workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=A.device)
+                if st != torch.cuda.current_stream(A.device).cuda_stream:
+                    # the caching allocator orders reuse against the allocating stream only:
+                    # tie the block to the stream the pack and the multiply run on, so that
+                    # it is not handed out again before they have finished
+                    workspace.record_stream(torch.cuda.ExternalStream(st, device=A.device))
             fn = gemm_bf16_ws if A.dtype == torch.bfloat16 else gemm_f16_ws
             s = fn(la[0], lb[0], M, N, K, alpha, A.data_ptr(), la[1], B.data_ptr(), lb[1],
                    beta, C.data_ptr(), ct, ldc, st, o, workspace.data_ptr(),
