@@ -176,6 +176,28 @@ gemm_status_t gemm_f16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t
                           float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
                           const gemm_opts_t* opts, void* workspace, size_t workspace_bytes);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): gemm_bf16_ws (in_type GEMM_BF16) or
+ * gemm_f16_ws (GEMM_F16) with the workspace taken from a static device array of the
+ * library, GEMM_STATIC_WS_BYTES per GPU (held by each GPU the library runs on until the
+ * process ends), instead of a caller buffer.  Allocates nothing: no hipMalloc / hipFree,
+ * no allocating library call.  A, B, C, the other arguments, the result and the k order
+ * are exactly those of gemm_*_ws given a large enough workspace.
+ * Every call on one GPU shares that GPU's array: calls that may overlap on one GPU
+ * (different streams, different host threads without ordering) race on it and must be
+ * serialised by the caller.  Its contents carry over between calls; a call rewrites every
+ * byte it reads, so stale contents never reach a result.
+ * Errors: as gemm_*_ws (checks run before anything is enqueued), plus
+ *   GEMM_ERR_INVALID_ARG -- in_type not bf16 / f16;
+ *   GEMM_ERR_UNSUPPORTED -- the rewritten operands need more than GEMM_STATIC_WS_BYTES
+ *       (gemm_workspace_size reports the bytes; use gemm_*_ws with a caller workspace);
+ *   GEMM_ERR_HIP -- the array's device address could not be looked up, or a launch failed. */
+#define GEMM_STATIC_WS_BYTES 33554432
+gemm_status_t gemm_ws_static(gemm_dtype_t in_type, gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N,
+                             int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                             float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                             const gemm_opts_t* opts);
+
 /* Workspace bytes a gemm_*_ws call with these arguments needs in order to rewrite its
  * operands (0 when it would not rewrite any), and, if plan is not NULL, what that call
  * launches when given at least that many bytes (gemm_plan_t.packed says which operands

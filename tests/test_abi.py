@@ -379,3 +379,22 @@ def test_matmul_rejects_overlapping_c_before_any_launch():
         Bv = B if C.shape[1] == 8 else B[:, :1]
         with pytest.raises(ValueError, match="overlap"):
             lg.matmul(A, Bv, C=C)
+
+
+def test_static_workspace_entry_rejects_before_touching_the_device():
+    """gemm_ws_static: argument errors and a rewrite larger than the static array are
+    refused before any device call (so this runs without a GPU)."""
+    big = lg.gemm_ws_static(BF16, ROW, ROW, 8192, 8192, 8192, 1.0, A16, 8192, B16, 8192, 0.0, C16, BF16, 8192)
+    assert big == lg.GEMM_ERR_UNSUPPORTED and "static workspace" in lg.gemm_last_error()
+    s, n, _ = ws_size(BF16, BF16, ROW, ROW, 8192, 8192, 8192)
+    assert s == 0 and n > lg.GEMM_STATIC_WS_BYTES
+    assert lg.gemm_ws_static(F32, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F32, 64) == \
+        lg.GEMM_ERR_INVALID_ARG
+    assert lg.gemm_ws_static(BF16, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F16, 64) == \
+        lg.GEMM_ERR_INVALID_ARG
+    assert lg.gemm_ws_static(F16, ROW, ROW, -1, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F16, 64) == \
+        lg.GEMM_ERR_INVALID_ARG
+    assert lg.gemm_ws_static(BF16, ROW, ROW, 0, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F32, 64) == lg.GEMM_OK
+    # the irregular-tail workload fits
+    s, n, _ = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, lda=2049, beta=1.0)
+    assert s == 0 and 0 < n <= lg.GEMM_STATIC_WS_BYTES

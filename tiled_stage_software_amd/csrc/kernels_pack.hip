@@ -17,6 +17,8 @@
 //              LDS, read along r and written along c, so both global sides stay coalesced
 //              (LDS chunks XOR-swizzled, free of bank conflicts on both sides).
 // Columns c >= len are written as zeros.  The pass is bound by HBM bandwidth.
+#include <atomic>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -171,6 +173,32 @@ hipError_t launch_pack(PackParams p, hipStream_t st) {
     if (total > INT32_MAX) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pack_kernel, dim3((unsigned)total), dim3(kPackThreads), 0, st, p);
     return hipGetLastError();
+}
+
+// Workspace of gemm_ws_static: the rewritten operands of a call that may not allocate go
+// here.  Each GPU holds its own copy for the life of the process; every call on a GPU
+// reuses it (the pack writes every byte a multiply then reads, zero padding included, so
+// nothing needs clearing between calls).  In host code `scratch` names only a host-side
+// stand-in: kernels get the device address that hipGetSymbolAddress returns.
+static __device__ __align__(256) char scratch[kStaticWsBytes];
+
+hipError_t static_workspace(void** ptr) {
+    // one address per device, looked up with that device current the first time a call
+    // needs it (atomics: concurrent first calls look it up twice and agree)
+    static std::atomic<void*> addr[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    void* p = addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p || (reinterpret_cast<uintptr_t>(p) & 255)) return hipErrorInvalidSymbol;
+        addr[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace gemm

@@ -48,4 +48,10 @@ struct PackParams {
 };
 hipError_t launch_pack(PackParams p, hipStream_t st);
 
+// The library's own workspace for gemm_ws_static: a static device array of
+// kStaticWsBytes per GPU (256-byte aligned), for callers that cannot allocate.  *ptr =
+// its device address on the current device (looked up once per device).
+constexpr int64_t kStaticWsBytes = int64_t(32) << 20;
+hipError_t static_workspace(void** ptr);
+
 }  // namespace gemm

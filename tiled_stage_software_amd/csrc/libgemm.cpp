@@ -101,6 +101,7 @@ const Tile kMfmaStaged[] = {
 };
 
 constexpr int kLdsLimit = 163840;  // bytes of LDS one workgroup may allocate on gfx950
+static_assert(gemm::kStaticWsBytes == GEMM_STATIC_WS_BYTES, "static workspace size as the header states");
 
 template <size_t N>
 const Tile* find_tile(const Tile (&t)[N], int id) {
@@ -537,6 +538,37 @@ gemm_status_t gemm_f16_ws(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t
                           void* workspace, size_t workspace_bytes) {
     return half_entry_ws(gemm::DT_F16, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, opts,
                          workspace, workspace_bytes);
+}
+
+gemm_status_t gemm_ws_static(gemm_dtype_t in_type, gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N,
+                             int64_t K, float alpha, const void* A, int64_t lda, const void* B, int64_t ldb,
+                             float beta, void* C, gemm_dtype_t c_type, int64_t ldc, hipStream_t stream,
+                             const gemm_opts_t* opts) {
+    g_err[0] = 0;
+    if (in_type != GEMM_BF16 && in_type != GEMM_F16)
+        return fail(GEMM_ERR_INVALID_ARG, "in_type %d: gemm_ws_static takes bf16 or f16 inputs", (int)in_type);
+    if (c_type != GEMM_F32 && c_type != in_type)
+        return fail(GEMM_ERR_INVALID_ARG, "c_type %d not offered for in_type %d", (int)c_type, (int)in_type);
+    Problem q{(int)in_type, (int)c_type, (int)la, (int)lb, M, N, K, alpha, beta, A, B, C, lda, ldb, ldc};
+    gemm_status_t s = validate(q);
+    if (s != GEMM_OK) return s;
+    // plan on stand-in addresses first: the size check needs nothing from the device
+    PackPlan pp;
+    gemm_plan_t plan;
+    GemmParams gp;
+    s = plan_ws(q, opts, nullptr, &pp, &plan, &gp);
+    if (s != GEMM_OK) return s;
+    if (!(pp.a || pp.b)) return launch(q.in_type, plan, gp, stream);   // nothing to rewrite
+    const int64_t need = pp.a_bytes + pp.b_bytes;
+    if (need > gemm::kStaticWsBytes)
+        return fail(GEMM_ERR_UNSUPPORTED,
+                    "the rewritten operands need %lld bytes, the static workspace holds %lld "
+                    "(gemm_*_ws takes a caller workspace of any size)",
+                    (long long)need, (long long)gemm::kStaticWsBytes);
+    void* ws = nullptr;
+    const hipError_t e = gemm::static_workspace(&ws);
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "static workspace: %s", hipGetErrorString(e));
+    return run_ws(q, opts, ws, (size_t)gemm::kStaticWsBytes, stream);
 }
 
 gemm_status_t gemm_f32(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t N, int64_t K, float alpha,

@@ -27,12 +27,13 @@ GEMM_F32, GEMM_BF16, GEMM_F16 = 0, 1, 2
 GEMM_FLAG_NO_XCD_REMAP = 1
 GEMM_FLAG_EQUAL_LDS = 2
 GEMM_MAX_NSTAGE = 4
+GEMM_STATIC_WS_BYTES = 33554432
 
 KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: "mfma_staged", 5: "scale"}
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
-           "gemm_bf16_ws", "gemm_f16_ws", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_tune_ws",
+           "gemm_bf16_ws", "gemm_f16_ws", "gemm_ws_static", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_tune_ws",
            "gemm_schedule", "gemm_pipe_copy", "gemm_h2d_staged", "gemm_status_string", "gemm_last_error")
 
 
@@ -85,6 +86,8 @@ def load():
         for name in ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
                      "gemm_bf16_ws", "gemm_f16_ws"):
             getattr(lib, name).restype = i32
+        lib.gemm_ws_static.argtypes = [i32] + base + [i32, i64, vp, ctypes.POINTER(GemmOpts)]
+        lib.gemm_ws_static.restype = i32
         lib.gemm_workspace_size.argtypes = [i32, i32, i32, i32, i64, i64, i64, f32, vp, i64, vp, i64, f32, vp,
                                             i64, ctypes.POINTER(GemmOpts), ctypes.POINTER(ctypes.c_size_t),
                                             ctypes.POINTER(GemmPlan)]
@@ -159,6 +162,12 @@ def gemm_f16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, st
                 workspace=0, workspace_bytes=0) -> int:
     return load().gemm_f16_ws(la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream, _ref(opts),
                               workspace, workspace_bytes)
+
+
+def gemm_ws_static(in_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream=0, opts=None) -> int:
+    """gemm_bf16_ws / gemm_f16_ws with the library's static workspace (allocates nothing)."""
+    return load().gemm_ws_static(in_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, c_type, ldc, stream,
+                                 _ref(opts))
 
 
 def gemm_workspace_size(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, opts=None):
