@@ -79,7 +79,8 @@ typedef enum gemm_kernel {
     GEMM_KERNEL_AUTO = 0,
     GEMM_KERNEL_VALU_RING = 1,   /* fp32 VALU, direct global->LDS nStage ring (A row-major, B row-major) */
     GEMM_KERNEL_VALU_STAGED = 2, /* fp32 VALU, loads staged through registers, any layout / alignment */
-    GEMM_KERNEL_MFMA_RING = 3,   /* bf16/f16 MFMA, direct global->LDS nStage ring (A and B K-contiguous) */
+    GEMM_KERNEL_MFMA_RING = 3,   /* bf16/f16 MFMA, direct global->LDS nStage ring (A and B K-contiguous;
+                                    tile 30: row-major A of any pitch and row-major B, read as they are) */
     GEMM_KERNEL_MFMA_STAGED = 4, /* bf16/f16 MFMA, loads staged through registers, any layout / alignment */
     GEMM_KERNEL_SCALE = 5        /* C = beta*C only (K == 0 or alpha == 0) */
 } gemm_kernel_t;
@@ -153,8 +154,10 @@ gemm_status_t gemm_f16_ex(gemm_layout_t la, gemm_layout_t lb, int64_t M, int64_t
  * direct-to-LDS ring take operands it cannot read in place.  The ring copies 16-byte
  * chunks of K-contiguous rows straight into LDS, a whole K-slab at a time (the page
  * "Software Pipelining and Double Buffering", section "Multi-stage pipelines"; the
- * staged loads of the other kernels take any layout but pass through registers).  When
- * an operand is N- or M-contiguous (B row-major, A column-major), has a base or pitch
+ * staged loads of the other kernels take any layout but pass through registers).  A ring
+ * that reads the operands as they are needs no rewrite (row-major A and B: tile 30, which
+ * takes B's N-contiguous slabs as they lie and A through registers).  Otherwise, when an
+ * operand is N- or M-contiguous (B row-major, A column-major), has a base or pitch
  * off 16 bytes, or K is not a multiple of 64, that operand is first rewritten into the
  * workspace as K-contiguous rows of K' = K rounded up to a multiple of 64 elements, the
  * extra columns zero (they add +0 to every sum), by one bandwidth-bound pass enqueued on
@@ -266,8 +269,10 @@ gemm_status_t gemm_tune_ws(gemm_dtype_t in_type, gemm_dtype_t c_type, gemm_layou
  *   5 WRITE    staged kernels: registers of slab `slab` -> ring slot `slot`
  *   6 WAIT_LDS the wave's own LDS reads and writes have completed
  * kernel: GEMM_KERNEL_VALU_RING / MFMA_RING / VALU_STAGED / MFMA_STAGED; ksteps = k-steps
- * per slab (2, 4 or 8), plus 16 for a ring kernel that spreads the copy of each slab
- * over the k-steps (one part per k-step; its ISSUE events carry arg = part | (parts << 8)).
+ * per slab (2, 4 or 8), plus 16 * code for a ring kernel that splits the copy of each slab
+ * into parts (its ISSUE events carry arg = part | (parts << 8)): code 0 = the whole copy at
+ * the slab's first k-step, 1 = one part per k-step, c >= 2 = c - 1 parts (at most one per
+ * k-step), the first issued right after the barrier that frees the slot.
  * Returns the number of events (writes at most `capacity` of them), or -1 for bad
  * arguments. */
 int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, int capacity);

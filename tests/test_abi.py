@@ -129,12 +129,16 @@ def test_plans_for_the_workloads():
     # f16 MLP shape NT
     s, p = plan(F16, F16, ROW, COL, 16384, 14336, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 56
-    # bf16 4000x3000x2049 NN, fp32 C: odd K and lda -> staged loader without a workspace;
-    # with one, the 192x256 split-copy tile on the rewritten operands (252 tiles, one round)
+    # bf16 4000x3000x2049 NN, fp32 C: odd K and lda, row-major B -> the 192x256 ring that reads
+    # row-major A (any pitch) and B as they are (252 tiles, one round), with or without a
+    # workspace; forcing the K-contiguous split tile rewrites both operands instead
     s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.tile == 30 and p.grid == 21 * 12
     s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.tile == 29 and p.grid == 21 * 12
+    assert s == 0 and n == 0 and p.tile == 30 and p.packed == 0
+    s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0, kernel=lg.GEMM_KERNEL_MFMA_RING,
+                      tile=29)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.tile == 29 and p.grid == 21 * 12 and p.packed == 3
 
 
 def test_ring_requirements_fall_back_to_staged():
@@ -252,13 +256,33 @@ def ws_size(in_t, c_t, la, lb, M, N, K, alpha=1.0, A=A16, lda=None, B=B16, ldb=N
 
 
 def test_workspace_size_of_the_irregular_workload():
-    # bf16 4000x3000x2049 NN: both operands rewritten, K padded to 2112
+    # bf16 4000x3000x2049 NN: read in place by tile 30, nothing to rewrite
     s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
+    assert s == 0 and n == 0 and p.packed == 0 and p.tile == 30
+    # with the split tile forced: both operands rewritten, K padded to 2112
+    s, n, p = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0, kernel=lg.GEMM_KERNEL_MFMA_RING,
+                      tile=29)
     assert s == 0 and p.packed == 3 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.bk in (32, 64)
     assert n == 4000 * 2112 * 2 + 3000 * 2112 * 2
-    # without a workspace the same call takes the staged kernel
-    s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED and p.packed == 0
+
+
+def test_row_major_ring_requirements():
+    """Tile 30 reads row-major A and B in place: any A pitch, K tail; B rows 16-byte
+    aligned and N a multiple of 8; enough tiles, else the staged kernel."""
+    args = dict(in_t=BF16, c_t=F32, la=ROW, lb=ROW, M=4000, N=3000, K=2049)
+    s, p = plan(**args)
+    assert s == 0 and p.tile == 30 and p.kernel == lg.GEMM_KERNEL_MFMA_RING
+    for kw in (dict(N=3004, ldb=3004), dict(ldb=3001), dict(B=B16 + 2), dict(M=500, N=500), dict(la=COL, lda=4000)):
+        a = dict(args)
+        a.update(kw)
+        s, p = plan(**a)
+        assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_STAGED, kw
+    s, p = plan(**dict(args, lda=2050, K=2050))
+    assert s == 0 and p.tile == 30
+    s, _ = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=30)
+    assert s == lg.GEMM_ERR_UNSUPPORTED and "row-major" in lg.gemm_last_error()
+    s, p = plan(**dict(args, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=30, nstage=1))
+    assert s == 0 and p.nstage == 1
 
 
 def test_workspace_size_rewrites_only_what_the_ring_cannot_read():
@@ -384,9 +408,9 @@ def test_matmul_rejects_overlapping_c_before_any_launch():
 def test_static_workspace_entry_rejects_before_touching_the_device():
     """gemm_ws_static: argument errors and a rewrite larger than the static array are
     refused before any device call (so this runs without a GPU)."""
-    big = lg.gemm_ws_static(BF16, ROW, ROW, 8192, 8192, 8192, 1.0, A16, 8192, B16, 8192, 0.0, C16, BF16, 8192)
+    big = lg.gemm_ws_static(BF16, COL, ROW, 8192, 8192, 8192, 1.0, A16, 8192, B16, 8192, 0.0, C16, BF16, 8192)
     assert big == lg.GEMM_ERR_UNSUPPORTED and "static workspace" in lg.gemm_last_error()
-    s, n, _ = ws_size(BF16, BF16, ROW, ROW, 8192, 8192, 8192)
+    s, n, _ = ws_size(BF16, BF16, COL, ROW, 8192, 8192, 8192)
     assert s == 0 and n > lg.GEMM_STATIC_WS_BYTES
     assert lg.gemm_ws_static(F32, ROW, ROW, 64, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F32, 64) == \
         lg.GEMM_ERR_INVALID_ARG
@@ -395,6 +419,7 @@ def test_static_workspace_entry_rejects_before_touching_the_device():
     assert lg.gemm_ws_static(F16, ROW, ROW, -1, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F16, 64) == \
         lg.GEMM_ERR_INVALID_ARG
     assert lg.gemm_ws_static(BF16, ROW, ROW, 0, 64, 64, 1.0, A16, 64, B16, 64, 0.0, C16, F32, 64) == lg.GEMM_OK
-    # the irregular-tail workload fits
-    s, n, _ = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, lda=2049, beta=1.0)
+    # the irregular-tail workload, rewritten for the split tile, fits
+    s, n, _ = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, lda=2049, beta=1.0,
+                      kernel=lg.GEMM_KERNEL_MFMA_RING, tile=29)
     assert s == 0 and 0 < n <= lg.GEMM_STATIC_WS_BYTES

@@ -67,6 +67,8 @@ FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= 
     ("f16", "f32", ROW, COL, K_MFMA_RING, 26, 2, 256, 512, 256),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 25, 4, 256, 256, 256),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 29, 1, 384, 256, 256),
+    ("bf16", "f32", ROW, ROW, K_MFMA_RING, 30, 2, 384, 512, 256),
+    ("f16", "f16", ROW, ROW, K_MFMA_RING, 30, 1, 256, 256, 256),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, 2, 200, 136, 77),
     ("f16", "f16", COL, ROW, K_MFMA_STAGED, 1, 1, 129, 257, 40),
 ]
@@ -165,12 +167,10 @@ def test_workload_small_vs_oracle(name):
     assert err <= TOL[cfg["dtype"]]
 
 
-@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4"])
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
 def test_workload_full_size_whole_matrix(name):
     """Full configuration sizes in the launch configuration the benchmark times: every
-    element against the oracle, the stated bar unadjusted (output rounding included).
-    (The irregular-tail workload runs through the workspace entry point, as the benchmark
-    launches it: tests/test_gpu_workspace.py.)"""
+    element against the oracle, the stated bar unadjusted (output rounding included)."""
     cfg = inputs.CONFIGS[name]
     p = inputs.make_problem(cfg)
     s, plan = lg.gemm_plan({"f32": 0, "bf16": 1, "f16": 2}[p.dtype], {"f32": 0, "bf16": 1, "f16": 2}[p.out],
@@ -200,6 +200,7 @@ FULL_STAGES = [  # (workload, kernel family, tile, stage counts): the default ti
     ("c2", K_VALU_RING, 5, [1, 2, 3, 4]),
     ("c3", K_MFMA_RING, 24, [1, 2]),
     ("c4", K_MFMA_RING, 24, [1, 2]),
+    ("c5", K_MFMA_RING, 30, [1, 2]),
 ]
 
 
@@ -238,6 +239,8 @@ RING_STAGES = [
     ("f16", "f16", ROW, COL, K_MFMA_RING, 23, [1, 2], 512, 768, 448),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 26, [1, 2], 768, 600, 576),
     ("bf16", "f32", ROW, COL, K_MFMA_RING, 29, [1, 2], 600, 768, 448),
+    ("bf16", "f32", ROW, ROW, K_MFMA_RING, 30, [1, 2], 600, 768, 449),
+    ("f16", "f16", ROW, ROW, K_MFMA_RING, 30, [1, 2], 400, 512, 384),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 19, [2, 3], 2304, 4352, 320),
     ("bf16", "f32", ROW, ROW, K_MFMA_STAGED, 1, [1, 2], 300, 200, 333),
     ("f32", "f32", COL, ROW, K_VALU_STAGED, 1, [1, 2], 300, 200, 77),
@@ -495,3 +498,37 @@ def test_valu_ring_on_ragged_edges(tile, S):
         p = problem("f32", "f32", M, N, K, ROW, ROW, dist="int2", seed=101, ldb=ldb)
         got = run(p, kernel=K_VALU_RING, tile=tile, nstage=S)
         assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
+
+
+# --------------------------------------------------------------- row-major A and B in place
+
+KN_CASES = [  # (dtype, out, M, N, K, lda pad, ldb pad, alpha, beta): K tails, odd A pitches, ragged M / N
+    ("bf16", "f32", 300, 512, 1, 0, 0, 1.0, 0.0),
+    ("bf16", "bf16", 193, 264, 17, 1, 8, 1.0, 0.0),
+    ("f16", "f16", 400, 520, 63, 3, 0, 1.0, 0.0),
+    ("bf16", "f32", 385, 256, 64, 0, 16, 0.5, 1.0),
+    ("f16", "f32", 600, 776, 65, 7, 0, -2.0, 0.5),
+    ("bf16", "bf16", 577, 1032, 130, 1, 24, 1.0, 0.0),
+    ("bf16", "f32", 4000, 3000, 2049, 0, 0, 0.5, 1.0),
+]
+
+
+@pytest.mark.parametrize("case", KN_CASES, ids=lambda c: f"{c[0]}-{c[1]}-{c[2]}x{c[3]}x{c[4]}")
+def test_row_major_ring_exact_on_tails_and_pitches(case):
+    """Tile 30 reads row-major A (any pitch, through registers) and row-major B (copied as
+    [k][n] rows, fragments gathered by transposing LDS reads) as they are, K tail included:
+    exact on small integers, and the same bits as the split tile on operands rewritten
+    into a workspace (same k order per accumulator)."""
+    dtype, out, M, N, K, pa, pb, alpha, beta = case
+    p = problem(dtype, out, M, N, K, ROW, ROW, dist="int2", alpha=alpha, beta=beta, seed=7, lda=K + pa, ldb=N + pb)
+    for S in (1, 2):
+        say(f"[row-major ring] {case} nstage={S}")
+        got = run(p, kernel=K_MFMA_RING, tile=30, nstage=S)
+        assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
+    q = problem(dtype, out, M, N, K, ROW, ROW, dist="normal", alpha=alpha, beta=beta, seed=8, lda=K + pa, ldb=N + pb)
+    a = run(q, kernel=K_MFMA_RING, tile=30, nstage=2)
+    C, ldc = gpu_gemm(q, ws="auto", kernel=K_MFMA_RING, tile=29, nstage=2)
+    b = c_logical(C, M, N, ldc)
+    bits = torch.int32 if out == "f32" else torch.int16
+    assert torch.equal(a.view(bits), b.view(bits))
+    assert err_vs_oracle(q, a) <= TOL[dtype]

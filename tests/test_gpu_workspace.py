@@ -97,30 +97,34 @@ def test_identical_to_the_ring_on_operands_packed_by_torch():
 
 
 def test_irregular_tail_workload_full_size():
-    """The bf16 4000x3000x2049 NN workload with fp32 C, alpha 0.5, beta 1, as the
-    benchmark launches it: every element within the bf16 tolerance."""
+    """The bf16 4000x3000x2049 NN workload with fp32 C, alpha 0.5, beta 1: with a workspace
+    offered, the call reads the operands in place (tile 30, nothing rewritten); forcing the
+    split tile rewrites both operands into the workspace.  Both give the same bits, within
+    the bf16 tolerance on every element."""
     cfg = inputs.CONFIGS["c5"]
     p = inputs.make_problem(cfg)
     n, plan = plan_of(p)
     say(f"[ws c5] packed={plan.packed} bytes={n} tile={plan.tile} S={plan.nstage} grid={plan.grid}")
-    assert plan.packed == 3 and plan.kernel == K_MFMA_RING
-    assert n == 4000 * 2112 * 2 + 3000 * 2112 * 2
+    assert plan.packed == 0 and plan.kernel == K_MFMA_RING and plan.tile == 30 and n == 0
     got = run(p, ws="auto")
     assert not torch.isnan(got).any()
     e = whole_matrix(p, got)
     say(f"[ws c5] all rows: err {e:.3e}")
     assert e <= TOL["bf16"]
+    n29, plan29 = plan_of(p, kernel=K_MFMA_RING, tile=29)
+    assert plan29.packed == 3 and n29 == 4000 * 2112 * 2 + 3000 * 2112 * 2
+    packed = run(p, ws="auto", kernel=K_MFMA_RING, tile=29)
+    assert torch.equal(got.view(torch.int32), packed.view(torch.int32))
 
 
 def test_irregular_tail_workload_full_size_bit_identical_across_stage_counts():
-    """Full c5 shape through the workspace: the default tile at one and two ring slots
-    gives the same bits."""
+    """Full c5 shape through the workspace path (operands rewritten for the split tile):
+    one and two ring slots give the same bits."""
     p = inputs.make_problem(inputs.CONFIGS["c5"])
-    n, plan = plan_of(p)
     outs = []
     for S in (1, 2):
-        say(f"[ws c5 stages] tile={plan.tile} S={S}")
-        outs.append(run(p, ws="auto", kernel=K_MFMA_RING, tile=plan.tile, nstage=S))
+        say(f"[ws c5 stages] tile=29 S={S}")
+        outs.append(run(p, ws="auto", kernel=K_MFMA_RING, tile=29, nstage=S))
     assert torch.equal(outs[0].view(torch.int32), outs[1].view(torch.int32))
 
 

@@ -84,7 +84,10 @@ def simulate(events, S, numK, ksteps, staged):
 
 @pytest.mark.parametrize("kernel", [lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING])
 @pytest.mark.parametrize("S", [1, 2, 3, 4, 5])
-@pytest.mark.parametrize("ksteps,spread", [(2, 0), (4, 0), (8, 0), (2, 1), (4, 1), (8, 1)])
+# code: 0 = each slab's copy issued whole at its first k-step; 1 = one part per k-step;
+# c >= 2 = c - 1 parts, the first right after the barrier that frees the slot
+@pytest.mark.parametrize("ksteps,spread", [(2, 0), (4, 0), (8, 0), (2, 1), (4, 1), (8, 1),
+                                           (2, 2), (4, 2), (4, 3), (8, 2), (8, 3), (8, 5)])
 def test_ring_protocol(kernel, S, ksteps, spread):
     for numK in list(range(0, 12)) + [33, 40]:
         ev = lg.gemm_schedule(kernel, S, numK, ksteps + 16 * spread)
@@ -143,7 +146,7 @@ def test_bad_arguments():
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 6, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 3, 4, 4) is None
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 3) is None
-    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 2 + 32) is None
+    assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 2, 4, 2 + 16 * 4) is None   # 3 parts of 2 k-steps
     assert lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_STAGED, 2, 4, 4 + 16) is None
     assert lg.gemm_schedule(99, 2, 4, 4) is None
 
@@ -172,9 +175,10 @@ def _planted(events, kind):
     return ev
 
 
+@pytest.mark.parametrize("code", [1, 3])
 @pytest.mark.parametrize("kind", ["no_barrier", "wait_too_little", "wrong_slot", "no_wait_lds", "late_part"])
-def test_simulator_catches_planted_bugs(kind):
-    ev = lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 3, 8, 4 + 16)
+def test_simulator_catches_planted_bugs(kind, code):
+    ev = lg.gemm_schedule(lg.GEMM_KERNEL_MFMA_RING, 3, 8, 4 + 16 * code)
     simulate(ev, 3, 8, 4, staged=False)
     with pytest.raises(AssertionError):
         simulate(_planted(ev, kind), 3, 8, 4, staged=False)

@@ -76,12 +76,23 @@ __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 // 16-byte chunk c of LDS row r lives at chunk position c ^ swz(r).  For CPR = 8
 // (128-byte rows) and CPR = 4 (64-byte rows) the functions make any 8 or 16 consecutive
 // rows read at one logical chunk hit distinct banks, for both 128- and 256-byte LDS
-// phases; both have period 16 in r.  CPR other than 4 / 8: no swizzle.
+// phases; both have period 16 in r.  CPR = 32 (512-byte rows: a [k][n] tile of 256
+// 16-bit columns) serves the transposing fragment reads, each of which takes two
+// neighbouring chunks from each of four consecutive rows per 16 lanes: the XOR values
+// 0, 4, 10, 14 for r mod 4 = 0..3 put those 4 x 2 chunks (and the next 16 lanes' 4 x 2
+// chunks, two chunks further on) on distinct banks in both 128- and 256-byte phases;
+// period 4 in r.  Other CPR: no swizzle.
 template <int CPR>
 __host__ __device__ __forceinline__ constexpr int swz(int r) {
     if constexpr (CPR == 8) return (r & 7) ^ ((r >> 3) & 1);
     else if constexpr (CPR == 4) return ((r >> 1) ^ (r >> 2)) & 3;
+    else if constexpr (CPR == 32) return (4 * (r & 3)) ^ (r & 2);
     else return 0;
+}
+// Row period of swz<CPR> (the swizzle phases a loader must tell apart).
+template <int CPR>
+__host__ __device__ __forceinline__ constexpr int swz_period() {
+    return CPR == 32 ? 4 : 16;
 }
 
 // ---------------------------------------------------------------- tile order

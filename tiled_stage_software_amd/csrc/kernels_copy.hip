@@ -74,7 +74,7 @@ __global__ __launch_bounds__(kCopyThreads) void pipe_copy_kernel(const CopyParam
     ops.dst = p.dst + first * kCopySlab;
     ops.band = wave_id() * (CopyRingOps<S>::L * 1024);
     ops.voff = (uint32_t)(ops.band + lane_id() * 16);
-    gemm_sched::ring_mainloop<S, CopyRingOps<S>::KS, false>(ops, (int)n);
+    gemm_sched::ring_mainloop<S, CopyRingOps<S>::KS, 0>(ops, (int)n);
 }
 
 hipError_t launch_pipe_copy(int nstage, const CopyParams& p, int64_t grid, hipStream_t st) {

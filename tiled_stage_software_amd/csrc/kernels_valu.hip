@@ -182,7 +182,7 @@ void valu_ring_kernel(const GemmParams p) {
     // A row-major: LDS row m <- A[m][k0 .. k0+BK); B row-major: LDS row k <- B[k][n0 .. n0+BN).
     ops.la.init(p.A + (int64_t)m0 * p.lda * 4, p.lda * 4, BK * 4);
     ops.lb.init(p.B + (int64_t)n0 * 4, p.ldb * 4, (int64_t)BK * p.ldb * 4);
-    gemm_sched::ring_mainloop<S, Ops::KS, false>(ops, p.K / BK);
+    gemm_sched::ring_mainloop<S, Ops::KS, 0>(ops, p.K / BK);
     ops.epilogue(p, m0, n0, m_keep, n_keep);
 }
 

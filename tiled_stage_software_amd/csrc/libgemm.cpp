@@ -67,6 +67,7 @@ const Tile kMfmaRing[] = {
     {26, 256, 192, 64, 512, S1 | S2, 2, (256 + 192) * 64 * 2},    // tile 23's scheme, 4x2 waves of 64x96
     {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
     {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64, copies spread
+    {30, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 29 on row-major A (any pitch) and row-major B
 #ifdef GEMM_ALL_TILES  // variants that lose on every workload measured (built on request)
     {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies spread over the slab
     {5, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},     // copies spread
@@ -155,14 +156,35 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // epilogue stages through LDS after the K loop whatever the stage count.
 int static_lds(const Tile& t, int S, int kernel, int c_type) {
     int lds = S * t.stage_bytes;
-    const bool split = t.id == 21 || t.id == 23 || t.id == 24 || t.id == 25 || t.id == 27 || t.id == 29;
+    const bool split = t.id == 21 || t.id == 23 || t.id == 24 || t.id == 25 || t.id == 27 || t.id == 29 || t.id == 30;
     if (kernel == GEMM_KERNEL_MFMA_RING && split && c_type != gemm::DT_F32 && t.bn == 256 && lds < t.bm * t.bn * 2)
         lds = t.bm * t.bn * 2;
     return lds;
 }
 
+// Tiles of the matrix-core ring that read a row-major A and a row-major (N-contiguous) B
+// as they are: A through registers (any pitch or alignment, K tail zero-filled), B's
+// K-slabs copied straight into LDS as [k][n] rows and read back with transposing loads.
+bool kn_tile(int id) { return id == 30; }
+
+bool kn_ok(const Problem& q, const Tile& t, const char** why) {
+    if (q.in_type == gemm::DT_F32) { *why = "16-bit inputs only"; return false; }
+    if (!(q.la == GEMM_ROW_MAJOR && q.lb == GEMM_ROW_MAJOR)) { *why = "needs A and B row-major"; return false; }
+    if (!aligned16(q.B) || (q.ldb * 2) % 16) { *why = "B rows not 16-byte aligned"; return false; }
+    // the last column tile starts at N - bn, where B's 16-byte chunks must begin
+    if (q.N % 8) { *why = "N not a multiple of 8"; return false; }
+    if (q.K == 0) { *why = "K == 0"; return false; }
+    if (q.M < t.bm || q.N < t.bn) { *why = "problem smaller than the tile"; return false; }
+    // per-lane 32-bit offsets: a slab of B spans bk rows, a tile of A bm rows
+    if ((q.ldb * 2) * (t.bk + 1) >= (int64_t(1) << 31) || (q.lda * 2) * (t.bm + 1) >= (int64_t(1) << 31)) {
+        *why = "leading dimension too large"; return false;
+    }
+    return true;
+}
+
 // Can the direct global->LDS ring run this problem with this tile?
 bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
+    if (mfma && kn_tile(t.id)) return kn_ok(q, t, why);
     const int es = elem_size(q.in_type);
     const int vec = 16 / es;
     if (mfma) {
@@ -277,6 +299,12 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
                 }
             }
             const Tile* pick = opts.tile ? find_tile(kMfmaRing, opts.tile) : (many ? big : mid);
+            // row-major A and B: the ring that reads them in place, once its 192x256 tiles
+            // give at least a quarter of the compute units work (else the staged kernel)
+            const Tile* kn = find_tile(kMfmaRing, 30);
+            if (!opts.tile && q.la == GEMM_ROW_MAJOR && q.lb == GEMM_ROW_MAJOR &&
+                cdiv(q.M, kn->bm) * cdiv(q.N, kn->bn) >= 64 && kn_ok(q, *kn, &why))
+                pick = kn;
             if (pick && ring_ok(q, *pick, true, &why)) { kernel = GEMM_KERNEL_MFMA_RING; t = pick; }
             else {
                 kernel = GEMM_KERNEL_MFMA_STAGED;
@@ -380,6 +408,10 @@ bool operand_direct(const void* p, int layout, int want, int64_t ld) {
 gemm_status_t plan_ws(const Problem& q, const gemm_opts_t* o, void* ws, PackPlan* pp, gemm_plan_t* plan,
                       GemmParams* gp) {
     *pp = PackPlan();
+    // a ring that reads the operands as they are (row-major A and B included) needs no
+    // rewrite
+    if (choose(q, o, plan, gp) == GEMM_OK && plan->kernel == GEMM_KERNEL_MFMA_RING) return GEMM_OK;
+    g_err[0] = 0;
     const int kernel = o ? o->kernel : 0;
     const int64_t kp = round_up(q.K, kPackK);
     const bool candidate = q.in_type != gemm::DT_F32 && q.M > 0 && q.N > 0 && q.K > 0 && q.alpha != 0.0f &&
@@ -451,20 +483,25 @@ struct Recorder {
     void write(int slab, int slot) { push(5, slab, slot, 0); }
 };
 
-template <int S, int KS>
-void rec_ring(Recorder& r, int numK, int spread) {
-    if (spread) gemm_sched::ring_mainloop<S, KS, true>(r, numK);
-    else gemm_sched::ring_mainloop<S, KS, false>(r, numK);
+// parts: the PARTS of the ring template (0 = whole slab at the first k-step, 1..KS parts)
+template <int S, int KS, int P = 0>
+bool rec_ring(Recorder& r, int numK, int parts) {
+    if constexpr (P > KS) {
+        return false;
+    } else {
+        if (parts == P) { gemm_sched::ring_mainloop<S, KS, P>(r, numK); return true; }
+        return rec_ring<S, KS, P + 1>(r, numK, parts);
+    }
 }
 template <int S, int KS>
 void rec_staged(Recorder& r, int numK) { gemm_sched::staged_mainloop<S, KS>(r, numK); }
 
 template <int S>
-bool rec_ring_ks(Recorder& r, int ks, int numK, int spread) {
+bool rec_ring_ks(Recorder& r, int ks, int numK, int parts) {
     switch (ks) {
-        case 2: rec_ring<S, 2>(r, numK, spread); return true;
-        case 4: rec_ring<S, 4>(r, numK, spread); return true;
-        case 8: rec_ring<S, 8>(r, numK, spread); return true;
+        case 2: return rec_ring<S, 2>(r, numK, parts);
+        case 4: return rec_ring<S, 4>(r, numK, parts);
+        case 8: return rec_ring<S, 8>(r, numK, parts);
     }
     return false;
 }
@@ -748,20 +785,23 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
     if (num_k < 0 || capacity < 0 || (capacity > 0 && !events)) return -1;
     Recorder r;
     bool ok = false;
-    // ksteps = k-steps per slab, + 16 for a ring kernel that spreads each copy over the slab
-    const int cs = ksteps >> 4;
+    // ksteps = k-steps per slab (low 4 bits) + 16 * code: code 0 = each slab's copy issued
+    // whole at its first k-step, 1 = spread over all k-steps (one part per k-step), c >= 2 =
+    // split into c - 1 parts, the first right after the barrier that frees the slot
+    const int code = ksteps >> 4;
     ksteps &= 15;
-    if (cs > 1) return -1;
+    const int parts = code == 0 ? 0 : code == 1 ? ksteps : code - 1;
+    if (parts > ksteps) return -1;
     if (kernel == GEMM_KERNEL_VALU_RING || kernel == GEMM_KERNEL_MFMA_RING) {
         switch (nstage) {
-            case 1: ok = rec_ring_ks<1>(r, ksteps, num_k, cs); break;
-            case 2: ok = rec_ring_ks<2>(r, ksteps, num_k, cs); break;
-            case 3: ok = rec_ring_ks<3>(r, ksteps, num_k, cs); break;
-            case 4: ok = rec_ring_ks<4>(r, ksteps, num_k, cs); break;
-            case 5: ok = rec_ring_ks<5>(r, ksteps, num_k, cs); break;
+            case 1: ok = rec_ring_ks<1>(r, ksteps, num_k, parts); break;
+            case 2: ok = rec_ring_ks<2>(r, ksteps, num_k, parts); break;
+            case 3: ok = rec_ring_ks<3>(r, ksteps, num_k, parts); break;
+            case 4: ok = rec_ring_ks<4>(r, ksteps, num_k, parts); break;
+            case 5: ok = rec_ring_ks<5>(r, ksteps, num_k, parts); break;
         }
     } else if (kernel == GEMM_KERNEL_VALU_STAGED || kernel == GEMM_KERNEL_MFMA_STAGED) {
-        if (cs != 0) return -1;
+        if (code != 0) return -1;
         switch (nstage) {
             case 1: ok = rec_staged_ks<1>(r, ksteps, num_k); break;
             case 2: ok = rec_staged_ks<2>(r, ksteps, num_k); break;

@@ -50,14 +50,15 @@ constexpr int kBufferFlags = 0x00020000;
 // first row times the row pitch, less its immediate -- passed as the scalar offset, and a
 // per-lane part that depends only on the lane and on the swizzle phase of the copy's
 // first row (NP phases), so a handful of lane-offset registers serve all copies.
-template <int LR, int ROWB, int NW, bool SWZ>
+template <int LR, int ROWB, int NW, bool SWZ, bool ASM = false>
 struct DirectLoader {
     static constexpr int CPR = ROWB / 16;
     static constexpr int RPI = 64 / CPR;            // LDS rows per copy instruction
     static constexpr int IPW = LR / (RPI * NW);     // copies per wave per slab
     static constexpr int GROUP = 4;                 // copies per M0 value (immediates < 4 KiB)
-    // swizzle phases of a copy's first row (the swizzle has period 16 in the row index)
-    static constexpr int NP = SWZ ? (RPI >= 16 ? 1 : 16 / RPI) : 1;
+    // swizzle phases of a copy's first row (the swizzle's period in the row index)
+    static constexpr int PERIOD = swz_period<CPR>();
+    static constexpr int NP = SWZ ? (RPI >= PERIOD ? 1 : PERIOD / RPI) : 1;
     static_assert(ROWB % 16 == 0 && CPR >= 1 && CPR <= 64 && 64 % CPR == 0, "row bytes");
     static_assert(IPW >= 1 && IPW * RPI * NW == LR, "rows must split evenly over the waves");
     static_assert(RPI * ROWB == 1024, "one copy fills 1 KiB of LDS");
@@ -108,18 +109,62 @@ struct DirectLoader {
     __device__ __forceinline__ void issue_at(const char* g, LDS_AS char* lds_tile, int i0, int i1) const {
         const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, -1, kBufferFlags);
 #pragma unroll
+        for (int i = 0; i < IPW; ++i)
+            if (i >= i0 && i < i1) copy_one(i, g, rs, lds_tile);
+    }
+    // Copy i of a slab whose LDS row 0 / chunk 0 is at global address g (rs: the same as a
+    // buffer resource).
+    __device__ __forceinline__ void copy_one(int i, const char* g, __amdgpu_buffer_rsrc_t rs, LDS_AS char* lds_tile) const {
+        LDS_AS char* m0 = lds_tile + lds_wave + (i / GROUP) * (GROUP * 1024);
+        const uint32_t vo = vpat[i % NP];
+        if constexpr (ASM) {
+            const char* sa = g + soff[i];
+            switch (i % GROUP) {
+                case 0: copy_g<0>(sa, vo, m0); break;
+                case 1: copy_g<1024>(sa, vo, m0); break;
+                case 2: copy_g<2048>(sa, vo, m0); break;
+                default: copy_g<3072>(sa, vo, m0); break;
+            }
+        } else {
+            switch (i % GROUP) {
+                case 0: copy<0>(rs, vo, soff[i], m0); break;
+                case 1: copy<1024>(rs, vo, soff[i], m0); break;
+                case 2: copy<2048>(rs, vo, soff[i], m0); break;
+                default: copy<3072>(rs, vo, soff[i], m0); break;
+            }
+        }
+    }
+    // Copies [i0, i1) of slab `slab` when only its first `rows` LDS rows exist in global
+    // memory (a partial last slab): lanes whose row lies beyond copy as usual (their
+    // lanes of the instruction are switched off), the others write +0 into their 16 bytes
+    // of LDS instead, so the slab's missing rows add nothing to any sum.  The zero writes
+    // go through the LDS counter; the caller drains it before the barrier.
+    __device__ __forceinline__ void issue_rows(int slab, LDS_AS char* lds_tile, int i0, int i1, int rows) const {
+        const char* g = base + (int64_t)slab * slab_step;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)g, (short)0, -1, kBufferFlags);
+        const int w = lds_wave / (IPW * 1024);
+        const int lr = lane_id() / CPR;
+#pragma unroll
         for (int i = 0; i < IPW; ++i) {
             if (i >= i0 && i < i1) {
-                LDS_AS char* m0 = lds_tile + lds_wave + (i / GROUP) * (GROUP * 1024);
-                const uint32_t vo = vpat[i % NP];
-                switch (i % GROUP) {
-                    case 0: copy<0>(rs, vo, soff[i], m0); break;
-                    case 1: copy<1024>(rs, vo, soff[i], m0); break;
-                    case 2: copy<2048>(rs, vo, soff[i], m0); break;
-                    default: copy<3072>(rs, vo, soff[i], m0); break;
+                if ((w * IPW + i) * RPI + lr < rows) {
+                    copy_one(i, g, rs, lds_tile);
+                } else {
+                    LDS_AS char* m0 = lds_tile + lds_wave + (i / GROUP) * (GROUP * 1024);
+                    *reinterpret_cast<LDS_AS u32x4*>(m0 + (i % GROUP) * 1024 + lane_id() * 16) = u32x4{0u, 0u, 0u, 0u};
                 }
             }
         }
+    }
+    // The global form of the same copy: LDS[M0 + IMM + 16*lane] = global[sa + voff + IMM],
+    // 16 bytes per lane.  Written as inline asm so that the compiler neither waits on the LDS
+    // counter for it nor moves other M0 users between the M0 write and the copy; completion
+    // is tracked by the explicit vmcnt waits of the ring protocol.  One wait state after
+    // the M0 write before the copy reads it.
+    template <int IMM>
+    static __device__ __forceinline__ void copy_g(const char* sa, uint32_t voff, LDS_AS char* m0) {
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 offset:%3"
+                     :: "v"(voff), "s"(sa), "s"((uint32_t)(uintptr_t)m0), "n"(IMM) : "m0");
     }
 };
 
@@ -289,6 +334,87 @@ struct StagedLoader {
                     *reinterpret_cast<LDS_AS uint16_t*>(dst) = (uint16_t)elem(0, e);
                 }
             }
+        }
+    }
+};
+
+// ------------------------------------------------------------------------------------
+// Register-staged loader for a K-contiguous 16-bit operand of any alignment: LR rows of LC
+// k per slab, each thread moving CH 16-byte vectors.  Every vector is one buffer load of
+// 16 bytes at the element's own (2- or 4-byte aligned) offset, which the hardware serves
+// whole (checked on the GPU), with no branch on alignment or position: the loads of one
+// slab never wait for those of the previous one, and they leave the issuing wave at once.
+// The buffer range ends at the operand's last element, so nothing beyond it is read (a
+// dword that crosses that end comes back as zero: the last element of each row is loaded
+// again on its own for the partial last slab, and put back).  In the partial last slab the
+// columns beyond K are cleared in registers before the write, so they add +0 to every sum.
+template <int LR, int LC, int NT>
+struct RowLoader {
+    static constexpr int VE = 8;              // 16-bit elements per vector
+    static constexpr int VPR = LC / VE;       // vectors per row
+    static constexpr int CH = LR * VPR / NT;  // vectors per thread per slab
+    static constexpr int ROWB = LC * 2;       // bytes per LDS row
+    static_assert(CH >= 1 && CH * NT == LR * VPR, "slab must split evenly over the threads");
+    u32x4 v[CH];
+    uint32_t last[CH];    // partial slab: element K-1 of each vector's row
+    const char* base;     // row 0, column 0 of the tile (slab 0)
+    int64_t ld;           // elements
+    int K;                // columns that exist
+    int64_t end;          // bytes from `base` to the end of the operand's last element
+
+    // X: the operand; rows r0 .. r0+LR-1 of its M rows are this tile's (r0 + LR <= M).
+    __device__ __forceinline__ void init(const char* X, int64_t ld_, int r0, int K_, int M) {
+        base = X + (int64_t)r0 * ld_ * 2;
+        ld = ld_;
+        K = K_;
+        end = ((int64_t)(M - 1 - r0) * ld_ + K_) * 2;
+    }
+    __device__ __forceinline__ void coords(int j, int& r, int& c) const {
+        const int q = (int)threadIdx.x + j * NT;
+        r = q / VPR;
+        c = (q % VPR) * VE;
+    }
+    // Issue the loads of slab `slab` (partial: the slab holds column K-1 and ends past it).
+    __device__ __forceinline__ void load(int slab, bool partial) {
+        const int64_t s0 = (int64_t)slab * ROWB;
+        const int64_t left = end - s0;
+        const uint32_t nrec = left > 0x7fffffff ? 0x7fffffffu : (uint32_t)left;
+        const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void*)(base + s0), (short)0, (int)nrec, kBufferFlags);
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            int r, c;
+            coords(j, r, c);
+            v[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(((int64_t)r * ld + c) * 2), 0, 0);
+        }
+        if (partial) {
+#pragma unroll
+            for (int j = 0; j < CH; ++j) {
+                int r, c;
+                coords(j, r, c);
+                last[j] = __builtin_amdgcn_raw_buffer_load_b16(rs, (uint32_t)(((int64_t)r * ld + (K - 1) - slab * LC) * 2), 0, 0);
+            }
+        }
+    }
+    // Write the registers of slab `slab` into an LDS tile ([row][k], rows of ROWB bytes,
+    // 16-byte chunks swizzled by swz<ROWB / 16>); the loads must have completed.
+    __device__ __forceinline__ void write(LDS_AS char* lds_tile, int slab, bool partial) {
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+            int r, c;
+            coords(j, r, c);
+            u32x4 x = v[j];
+            if (partial) {
+                const int k0 = slab * LC + c;       // column of element 0
+#pragma unroll
+                for (int e = 0; e < VE; ++e) {
+                    const uint32_t sh = (e & 1) * 16;
+                    uint32_t w = x[e >> 1];
+                    if (k0 + e == K - 1) w = (w & ~(0xffffu << sh)) | ((last[j] & 0xffffu) << sh);
+                    else if (k0 + e >= K) w &= ~(0xffffu << sh);
+                    x[e >> 1] = w;
+                }
+            }
+            *reinterpret_cast<LDS_AS u32x4*>(lds_tile + lds_offset<ROWB, 2, true>(r, c)) = x;
         }
     }
 };

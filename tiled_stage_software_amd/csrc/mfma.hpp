@@ -407,7 +407,7 @@ void mfma_ring_kernel(const GemmParams p) {
     ops.init((LDS_AS char*)(smem_raw));
     ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
     ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-    gemm_sched::ring_mainloop<S, Ops::KS, SPREAD>(ops, p.K / BK);
+    gemm_sched::ring_mainloop<S, Ops::KS, SPREAD ? Ops::KS : 0>(ops, p.K / BK);
     ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
 }
 
@@ -468,7 +468,7 @@ void mfma_split_kernel(const GemmParams p) {
         ops.init((LDS_AS char*)(smem_raw));
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-        gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, BK / 16, SPREAD ? BK / 16 : 0>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
@@ -476,7 +476,7 @@ void mfma_split_kernel(const GemmParams p) {
     } else {
         SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false> ops;
         ops.init((LDS_AS char*)(smem_raw));
-        gemm_sched::ring_mainloop<S, BK / 16, SPREAD>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, BK / 16, SPREAD ? BK / 16 : 0>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
@@ -554,12 +554,12 @@ void mfma_splitp_kernel(const GemmParams p) {
         ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
         ops.la.init(p.A, p.lda * 2, BK * 2);
         ops.lb.init(p.B, p.ldb * 2, BK * 2);
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, nslabs);
     } else {
         SplitPersistOpsOut<T, OUT, BM, BN, BK, WM, WN, S, NC, false> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, nslabs);
     }
 }
 
@@ -581,6 +581,170 @@ template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, in
 static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
     hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD>), dim3(grid), dim3(WM * WN * 64),
+                       p.lds_pad, st, p);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------- row-major B in place
+// B (K x N) row-major is N-contiguous.  Its K-slab is copied into LDS as it lies -- BK rows
+// (one per k) of BN elements, 16-byte chunk c of row r at chunk position c ^ swz<BN/8>(r)
+// -- and each lane gathers its B fragment (8 consecutive k of one column) with two
+// transposing LDS reads, ds_read_b64_tr_b16: within each group of 16 lanes the instruction
+// treats the 8-byte pieces the 16 lanes address as a 16 x 4 block and hands lane i
+// element i mod 4 of the pieces addressed by lanes i/4, i/4 + 4, i/4 + 8, i/4 + 12.  Lane j
+// of a group therefore points at row kb + j/4, columns nb + 4(j mod 4) .. +3, and lane i
+// receives B[kb .. kb+3][nb + i]; rows kb + 4 .. kb + 7 give the other half.  The fragment
+// a lane of the 32x32x16 instruction needs -- column l mod 32, k-chunk l / 32 -- sets
+// kb = 8 (g / 2) and nb = 16 (g mod 2) for lane group g = l / 16.  (Layout checked on the
+// GPU with a one-wave probe.)  A keeps the K-contiguous [m][k] tile.
+template <typename T, int BM, int BN, int BK, int WM, int WN>
+struct MfmaKnCompute : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN, 32> C;
+    static constexpr int ROWB_B = BN * 2;   // bytes per k-row of the B tile
+    static constexpr int CPR_B = ROWB_B / 16;
+    static_assert(CPR_B == 32, "the transposing reads are laid out for 256-column B tiles");
+    static_assert(C::B_BYTES == BK * ROWB_B, "same B bytes per slot in either layout");
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    uint32_t btr[C::TN];   // per lane: byte offset of the piece it addresses for fragment j
+                           // (k-step 0, rows kb .. kb+3), relative to the slot
+
+    __device__ __forceinline__ void init(LDS_AS char* smem_) {
+        C::init(smem_);
+        const int wn = wave_id() % WN;
+        const int lane = lane_id();
+        const int g = lane / 16, j16 = lane % 16;
+        // the k row this lane addresses: rows of one read differ by multiples of 4 from it,
+        // so its swizzle phase (row mod 4) is the same for every k-step and half
+        const int r = 8 * (g / 2) + j16 / 4;
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            const int n = wn * C::WTN + j * 32 + 16 * (g % 2) + 4 * (j16 % 4);
+            btr[j] = (uint32_t)(C::A_BYTES + r * ROWB_B + (((n >> 3) ^ swz<CPR_B>(r)) << 4) + (n & 7) * 2);
+        }
+    }
+
+    template <int BUF>
+    __device__ __forceinline__ void frag(int slot, int ks) {
+        LDS_AS const char* st = this->smem + slot * C::STAGE;
+#pragma unroll
+        for (int i = 0; i < C::TM; ++i)
+            this->fa[BUF][i] = *reinterpret_cast<LDS_AS const typename C::frag_t*>(st + this->a_off[ks] + i * 32 * C::ROWB);
+#pragma unroll
+        for (int j = 0; j < C::TN; ++j) {
+            LDS_AS const char* b = st + btr[j] + ks * 16 * ROWB_B;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS_AS s16x4*)(b + 4 * ROWB_B));
+            this->fb[BUF][j] = __builtin_bit_cast(typename C::frag_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        }
+    }
+};
+
+// Split-copy ring over a row-major A of any alignment and a row-major B read in place.
+// The copying waves (one per SIMD) bring each K-slab in two ways: B's BK rows by direct
+// global->LDS copies (16-byte aligned rows, spread over the slab like the other split
+// tiles); A's BM rows through registers, with 16-byte loads of any alignment issued as
+// soon as the slot is free and written into it just before the barrier that publishes the
+// slab (the staged half of the protocol).  A K tail needs no padding: A's columns beyond K
+// are cleared in registers, and in the last, partial slab the lanes of B's copies whose
+// rows lie beyond K write +0 into LDS instead of copying, so those k add +0 to every sum,
+// as in zero-padded operands.  The B copies are issued as inline asm (the global form of
+// the LDS-bound load), out of the compiler's sight: it would otherwise make every
+// transposing fragment read wait for all copies in flight; the protocol's own vmcnt waits
+// and barriers order them.
+template <typename T, int BM, int BN, int BK, int WM, int WN, int NC, bool COPY>
+struct KnSplitOps : MfmaKnCompute<T, BM, BN, BK, WM, WN> {
+    typedef MfmaKnCompute<T, BM, BN, BK, WM, WN> C;
+    static constexpr int NTC = NC * 64;                        // copying threads (waves 0..NC-1)
+    RowLoader<BM, BK, NTC> la;                                 // A: [m][k] rows, any alignment
+    DirectLoader<BK, BN * 2, NC, true, true> lb;               // B: [k][n] rows
+    static constexpr int LB = DirectLoader<BK, BN * 2, NC, true, true>::IPW;
+    int numK = 0;
+    int k_last = BK;          // rows (k) of the last slab that exist
+    int pend_slot = 0;        // slot the register-staged A of the next slab goes to
+    int pend_slab = 0;
+
+    __device__ __forceinline__ bool partial(int slab) const { return slab == numK - 1 && k_last < BK; }
+    __device__ __forceinline__ void issue(int slab, int slot, int part, int parts) {
+        if (!COPY) return;
+        if (part == 0) {
+            la.load(slab, partial(slab));
+            pend_slot = slot;
+            pend_slab = slab;
+        }
+        LDS_AS char* st = this->smem + slot * C::STAGE + C::A_BYTES;
+        const int i0 = part * LB / parts, i1 = (part + 1) * LB / parts;
+        if (partial(slab)) lb.issue_rows(slab, st, i0, i1, k_last);
+        else lb.issue(slab, st, i0, i1);
+    }
+    // Two slots at most: every copy and load in flight belongs to the next slab, which the
+    // wait completes; A's registers are then written into its slot (their loads have had
+    // the whole slab to arrive: writing them earlier, mid-slab, measured slower), and the
+    // LDS counter drained so the barrier that follows publishes them.
+    template <int N>
+    __device__ __forceinline__ void wait_slabs() {
+        static_assert(N == 0, "one slab in flight at most");
+        if (!COPY) return;
+        wait_vm<0>();
+        la.write(this->smem + pend_slot * C::STAGE, pend_slab, partial(pend_slab));
+        wait_lgkm0();
+    }
+    __device__ __forceinline__ void wait_lds() { wait_lgkm0(); }
+    __device__ __forceinline__ void barrier() { gemm::barrier(); }
+    template <int BUF>
+    __device__ __forceinline__ void frag(int, int slot, int ks) { C::template frag<BUF>(slot, ks); }
+    template <int BUF, int HAS, int PARTS>
+    __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (LB + PARTS - 1) / PARTS : 0>(); }
+};
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
+void mfma_kn_kernel(const GemmParams p) {
+    static_assert(S == 1 || S == 2, "the staged half of the protocol holds one slab in registers");
+    static constexpr int STAGE = (BM + BN) * BK * 2;
+    static constexpr int EPI = (OUT != DT_F32 && BN == 256) ? BM * BN * 2 : 0;
+    static constexpr int SMEM = S * STAGE > EPI ? S * STAGE : EPI;
+    __shared__ __attribute__((aligned(1024))) char smem_raw[SMEM];
+    int tm, tn;
+    tile_coords(p, tm, tn);
+    // edge tiles shifted inward, as in the other ring kernels (the host guarantees M >= BM,
+    // N >= BN); the K range is covered whole, the last slab possibly partial
+    const int m_keep = tm * BM, n_keep = tn * BN;
+    const int m0 = min(m_keep, p.M - BM);
+    const int n0 = min(n_keep, p.N - BN);
+    const int numK = (p.K + BK - 1) / BK;
+    const int k_last = p.K - (numK - 1) * BK;
+    constexpr bool LDS_EPI = EPI > 0;
+    const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
+                         n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
+    constexpr int KS = BK / 16;
+    if (wave_id() < NC) {
+        KnSplitOps<T, BM, BN, BK, WM, WN, NC, true> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.numK = numK;
+        ops.k_last = k_last;
+        ops.la.init(p.A, p.lda, m0, p.K, p.M);
+        ops.lb.init(p.B + (int64_t)n0 * 2, p.ldb * 2, (int64_t)BK * p.ldb * 2);
+        gemm_sched::ring_mainloop<S, KS, S == 1 ? 0 : KS>(ops, numK);
+        if constexpr (LDS_EPI) {
+            if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
+        }
+        ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+    } else {
+        KnSplitOps<T, BM, BN, BK, WM, WN, NC, false> ops;
+        ops.init((LDS_AS char*)(smem_raw));
+        ops.numK = numK;
+        gemm_sched::ring_mainloop<S, KS, S == 1 ? 0 : KS>(ops, numK);
+        if constexpr (LDS_EPI) {
+            if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
+        }
+        ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
+    }
+}
+
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+static hipError_t launch_kn(const GemmParams& p, hipStream_t st) {
+    const int grid = p.tiles_m * p.tiles_n;
+    hipLaunchKernelGGL((mfma_kn_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC>), dim3(grid), dim3(WM * WN * 64),
                        p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -648,11 +812,11 @@ void mfma_ws_kernel(const GemmParams p) {
         ops.smem = (LDS_AS char*)(smem_raw);
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2, wave_id() - 4);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2, wave_id() - 4);
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, numK);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, numK);
     } else {
         WsConsumerOps<T, BM, BN, BK> ops;
         ops.init((LDS_AS char*)(smem_raw));
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, numK);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, numK);
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     }
 }
@@ -723,12 +887,12 @@ void mfma_wsp_kernel(const GemmParams p) {
         ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
         ops.la.init(p.A, p.lda * 2, BK * 2, wave_id() - 4);
         ops.lb.init(p.B, p.ldb * 2, BK * 2, wave_id() - 4);
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, nslabs);
     } else {
         WspConsumerOps<T, OUT, BM, BN, BK> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.gp = &p; ops.numK = numK; ops.wg = wg; ops.G = G;
-        gemm_sched::ring_mainloop<S, BK / 16, false>(ops, nslabs);
+        gemm_sched::ring_mainloop<S, BK / 16, 0>(ops, nslabs);
     }
 }
 
@@ -859,6 +1023,10 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             break;
         case 28:  // tile 23, persistent (one workgroup per CU walks several tiles through one ring)
             if (S == 2) return launch_splitp<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
+            break;
+        case 30:  // 192x256x64, 2x4 waves of 96x64: row-major A through registers, row-major B in place
+            if (S == 1) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
+            if (S == 2) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
             break;
         case 29:  // tile 27 (192x256) with each slab's copies spread over the k-steps
             if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true>(p, st);

@@ -52,26 +52,27 @@ enum { BODY_MAIN = 0, BODY_MAIN_END = 1, BODY_TAIL = 2, BODY_LAST = 3 };
 // body is straight-line code (a run-time branch inside it lets the compiler sink the
 // math below it and keep every fragment of the slab live at once).
 //
-// SPREAD = false: the whole copy of slab kt+S-1 is issued at the first k-step.
-// SPREAD = true:  the copy is split into KS parts, one per k-step: part 0 right after
-//   the barrier that ends slab kt-1 (that barrier frees the slot), parts 1..KS-1 at
-//   k-steps 0..KS-2 of slab kt.  The copies then trickle out at the rate the texture
-//   path drains them instead of backing up the wave's issue, and every part is still
-//   issued before the wait that counts it.
-//   BODY_MAIN:     issues (its parts of) slab kt+S-1 and, with SPREAD, part 0 of slab
+// PARTS = 0: the whole copy of slab kt+S-1 is issued at the first k-step.
+// PARTS = P in 1..KS: the copy is split into P parts: part 0 right after the barrier that
+//   ends slab kt-1 (that barrier frees the slot), parts 1..P-1 at k-steps 0..P-2 of slab
+//   kt.  With P = KS the copies trickle out at the rate the texture path drains them
+//   instead of backing up the wave's issue; with P = 1 the whole slab goes out at the
+//   earliest point the slot allows.  Every part is issued before the wait that counts it.
+//   BODY_MAIN:     issues (its parts of) slab kt+S-1 and, with PARTS > 0, part 0 of slab
 //                  kt+S after its barrier; waits for slab kt+1 leaving S-2 slabs in flight.
 //   BODY_MAIN_END: the last slab that issues: no part 0 of a next slab.
 //   BODY_TAIL:     nothing left to issue; waits for everything in flight.
 //   BODY_LAST:     the last slab: no copy, no barrier, no read-ahead.
-template <int S, int KS, bool SPREAD, int BODY, class Ops>
+template <int S, int KS, int PARTS, int BODY, class Ops>
 GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot) {
+    static_assert(PARTS >= 0 && PARTS <= KS, "at most one part per k-step");
     constexpr bool ISSUING = BODY == BODY_MAIN || BODY == BODY_MAIN_END;
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
         int copies_here = 0;  // parts issued in this k-step (for the math's interleave)
         if (ISSUING) {
-            if (!SPREAD && ks == 0) { ops.issue(kt + S - 1, issue_slot, 0, 1); copies_here = KS; }
-            if (SPREAD && ks < KS - 1) { ops.issue(kt + S - 1, issue_slot, ks + 1, KS); copies_here = 1; }
+            if (PARTS == 0 && ks == 0) { ops.issue(kt + S - 1, issue_slot, 0, 1); copies_here = KS; }
+            if (PARTS > 0 && ks < PARTS - 1) { ops.issue(kt + S - 1, issue_slot, ks + 1, PARTS); copies_here = 1; }
         }
         if (ks == KS - 1) {
             if (BODY != BODY_LAST) {
@@ -80,7 +81,7 @@ GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot
                 ops.barrier();
                 ops.template frag<0>(kt + 1, next_slot, 0);
                 // the barrier freed this slab's slot: start the copy of slab kt+S into it
-                if (SPREAD && BODY == BODY_MAIN) { ops.issue(kt + S, slot, 0, KS); copies_here = 1; }
+                if (PARTS > 0 && BODY == BODY_MAIN) { ops.issue(kt + S, slot, 0, PARTS); copies_here = PARTS == 1 ? KS : 1; }
             }
         } else {
             if (ks % 2 == 0) ops.template frag<1>(kt, slot, ks + 1);
@@ -91,8 +92,9 @@ GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot
             if (ks % 2 == 0) ops.template math<0, 1, 1>(ks);
             else ops.template math<1, 1, 1>(ks);
         } else if (copies_here == 1) {
-            if (ks % 2 == 0) ops.template math<0, 1, KS>(ks);
-            else ops.template math<1, 1, KS>(ks);
+            constexpr int P = PARTS > 0 ? PARTS : 1;   // (PARTS == 0 never gets here)
+            if (ks % 2 == 0) ops.template math<0, 1, P>(ks);
+            else ops.template math<1, 1, P>(ks);
         } else {
             if (ks % 2 == 0) ops.template math<0, 0, 1>(ks);
             else ops.template math<1, 0, 1>(ks);
@@ -115,7 +117,7 @@ GEMM_HD void single_slab_compute(Ops& ops, int kt) {
     }
 }
 
-// Direct global->LDS ring.  KS = k-steps per slab (even); SPREAD: see ring_slab.
+// Direct global->LDS ring.  KS = k-steps per slab (even); PARTS: see ring_slab.
 // Hook after slab kt's last k-step (a persistent kernel stores a finished tile there);
 // Ops without an after_slab member do nothing.
 template <class O>
@@ -123,7 +125,7 @@ GEMM_HD auto after_slab_(O& o, int kt, int) -> decltype(o.after_slab(kt), void()
 template <class O>
 GEMM_HD void after_slab_(O&, int, long) {}
 
-template <int S, int KS, bool SPREAD, class Ops>
+template <int S, int KS, int PARTS, class Ops>
 GEMM_HD void ring_mainloop(Ops& ops, int numK) {
     static_assert(KS % 2 == 0, "fragment double-buffering needs an even number of k-steps");
     static_assert(S >= 1, "at least one LDS slot");
@@ -146,33 +148,33 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
         else ops.template wait_slabs<0>();
         ops.barrier();
         ops.template frag<0>(0, 0, 0);
-        // SPREAD: part 0 of slab S-1 goes into the still unused slot S-1
-        if (SPREAD && numK > S - 1) ops.issue(S - 1, S - 1, 0, KS);
+        // PARTS > 0: part 0 of slab S-1 goes into the still unused slot S-1
+        if (PARTS > 0 && numK > S - 1) ops.issue(S - 1, S - 1, 0, PARTS);
         int kt = 0;
         int slot = 0;            // slot of slab kt
         int issue_slot = S - 1;  // slot of slab kt+S-1 (= the slot slab kt-1 used)
         const int main_end = numK - S + 1;  // slabs whose body still issues a copy
         for (; kt < main_end - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, SPREAD, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
+            ring_slab<S, KS, PARTS, BODY_MAIN>(ops, kt, slot, issue_slot, next_slot);
             after_slab_(ops, kt, 0);
             slot = next_slot;
             issue_slot = (issue_slot + 1 == S) ? 0 : issue_slot + 1;
         }
         if (kt < main_end) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, SPREAD, BODY_MAIN_END>(ops, kt, slot, issue_slot, next_slot);
+            ring_slab<S, KS, PARTS, BODY_MAIN_END>(ops, kt, slot, issue_slot, next_slot);
             after_slab_(ops, kt, 0);
             slot = next_slot;
             ++kt;
         }
         for (; kt < numK - 1; ++kt) {
             const int next_slot = (slot + 1 == S) ? 0 : slot + 1;
-            ring_slab<S, KS, SPREAD, BODY_TAIL>(ops, kt, slot, 0, next_slot);
+            ring_slab<S, KS, PARTS, BODY_TAIL>(ops, kt, slot, 0, next_slot);
             after_slab_(ops, kt, 0);
             slot = next_slot;
         }
-        ring_slab<S, KS, SPREAD, BODY_LAST>(ops, kt, slot, 0, 0);
+        ring_slab<S, KS, PARTS, BODY_LAST>(ops, kt, slot, 0, 0);
         after_slab_(ops, kt, 0);
     }
 }
