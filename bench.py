@@ -227,9 +227,51 @@ def h2d_staging_control(dev, mib: int = 256, chunk_mib: int = 4, reps: int = 3):
         host.to(dev)
     torch.cuda.synchronize()
     ref = n / ((time.perf_counter() - t0) / reps) / 1e9
+    overlap = h2d_gemm_overlap(dev, src, dst)
     del dst
     return {"what": f"{mib} MiB pageable host -> device through nStage page-locked slots of {chunk_mib} MiB",
-            "nstage": out, "copy_exact": ok, "torch_pageable_copy_GB/s": round(ref, 2)}
+            "nstage": out, "copy_exact": ok, "torch_pageable_copy_GB/s": round(ref, 2), "overlap_with_gemm": overlap}
+
+
+def h2d_gemm_overlap(dev, src: np.ndarray, dst: torch.Tensor, chunk_mib: int = 4, gemms: int = 80):
+    """Wall time of `gemms` bf16 4096^3 NT GEMMs queued on one stream, of the asynchronous
+    two-slot staged copy of `src` on another, and of both together (GEMMs queued first,
+    then the copy; both streams synchronised): overlap = (alone + alone - together) /
+    the shorter of the two (1 = the shorter hides entirely behind the longer)."""
+    n = src.size
+    chunk = chunk_mib << 20
+    p = inputs.make_problem(inputs.CONFIGS["c3"], M=4096, N=4096, K=4096)
+    A, B = p.A.storage.to(dev), p.B.storage.to(dev)
+    C = torch.empty(4096 * 4096, dtype=torch.bfloat16, device=dev)
+    g, h = torch.cuda.Stream(dev), torch.cuda.Stream(dev)
+    staging = torch.empty(2 * chunk, dtype=torch.uint8, pin_memory=True)
+
+    def launch_gemms():
+        for _ in range(gemms):
+            lg.check(lg.gemm_bf16(inputs.ROW, inputs.COL, 4096, 4096, 4096, 1.0, A.data_ptr(), 4096, B.data_ptr(),
+                                  4096, 0.0, C.data_ptr(), lg.GEMM_BF16, 4096, g.cuda_stream))
+
+    def copy():
+        lg.check(lg.gemm_h2d_staged_async(dst.data_ptr(), src.ctypes.data, n, staging.data_ptr(), chunk, 2,
+                                          h.cuda_stream))
+
+    def wall(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        fn()
+        g.synchronize()
+        h.synchronize()
+        return (time.perf_counter() - t0) * 1e3
+    wall(launch_gemms)
+    wall(copy)
+    tg = min(wall(launch_gemms) for _ in range(3))
+    th = min(wall(copy) for _ in range(3))
+    tb = min(wall(lambda: (launch_gemms(), copy())) for _ in range(3))
+    exact = bool(np.array_equal(dst.cpu().numpy(), src))
+    del A, B, C, staging
+    return {"what": f"{gemms} bf16 4096^3 GEMMs on one stream, {n >> 20} MiB staged host copy (2 slots, "
+                    f"asynchronous call) on another", "gemm_ms": round(tg, 3), "h2d_ms": round(th, 3),
+            "together_ms": round(tb, 3), "overlap": round((tg + th - tb) / min(tg, th), 3), "copy_exact": exact}
 
 
 def cpu_model() -> str:

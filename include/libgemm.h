@@ -307,6 +307,18 @@ gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nsta
 gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
                               int nstage, hipStream_t stream);
 
+/* gemm_h2d_staged without the final wait: returns once every chunk has been copied into
+ * the staging ring and its DMA enqueued on `stream`, with up to min(nstage, chunks) DMAs
+ * still running.  The CPU's part of the copy and the GPU's work on other streams overlap
+ * as before; what the caller gains is the host thread, free as soon as the last chunk is
+ * staged (the page's CPU/GPU overlap, with the ring's last slots drained by the stream).
+ * Contract: `staging` (and `dst`) must stay untouched until `stream` has passed the copies
+ * (hipStreamSynchronize(stream), or an event recorded on `stream` after this call).
+ * Arguments and errors as gemm_h2d_staged; after an error the call waits for any DMA it
+ * enqueued. */
+gemm_status_t gemm_h2d_staged_async(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
+                                    int nstage, hipStream_t stream);
+
 const char* gemm_status_string(gemm_status_t status);
 
 /* Thread-local description of the last non-OK status on this thread ("" if none). */

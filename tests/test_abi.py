@@ -352,7 +352,9 @@ def test_h2d_staged_rejects_bad_arguments_before_copying():
                        ((A16, H, 8192, 0, 4096, 2), lg.GEMM_ERR_INVALID_ARG),
                        ((A16, H, 8192, H + 4096, 4096, 2), lg.GEMM_ERR_INVALID_ARG)):  # src overlaps the ring
         assert lg.gemm_h2d_staged(*args) == want, args
+        assert lg.gemm_h2d_staged_async(*args) == want, args
     assert lg.gemm_h2d_staged(A16, H, 0, H + (1 << 20), 4096, 2) == lg.GEMM_OK   # nothing to copy
+    assert lg.gemm_h2d_staged_async(A16, H, 0, H + (1 << 20), 4096, 2) == lg.GEMM_OK
 
 
 # --------------------------------------------------------------- failure paths without a GPU

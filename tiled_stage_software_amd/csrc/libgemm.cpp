@@ -839,8 +839,16 @@ gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nsta
     return GEMM_OK;
 }
 
-gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
-                              int nstage, hipStream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// The host-side ring behind gemm_h2d_staged / gemm_h2d_staged_async: the CPU fills
+// page-locked slot c mod nstage with chunk c while the DMA engine drains the slots filled
+// before; a slot is refilled only once the DMA that read it has completed (one event per
+// slot).  drain: wait for the last DMAs too before returning.
+gemm_status_t h2d_ring(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes, int nstage,
+                       hipStream_t stream, bool drain) {
     g_err[0] = 0;
     if (bytes < 0) return fail(GEMM_ERR_INVALID_ARG, "bytes %lld < 0", (long long)bytes);
     if (nstage < 1 || nstage > 4) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d: the staging ring has 1..4 slots", nstage);
@@ -851,7 +859,6 @@ gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* s
     const char* g0 = static_cast<const char*>(staging);
     const int64_t ring = chunk_bytes * nstage;
     if (s0 < g0 + ring && g0 < s0 + bytes) return fail(GEMM_ERR_INVALID_ARG, "src and staging overlap");
-    // one event per slot: the DMA that last read the slot has finished when it completes
     hipEvent_t ev[4];
     int made = 0;
     gemm_status_t result = GEMM_OK;
@@ -876,15 +883,31 @@ gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* s
         if (e == hipSuccess) e = hipEventRecord(ev[slot], stream);  // ... while the DMA drains the others
         if (e != hipSuccess) { result = fail(GEMM_ERR_HIP, "staged copy failed: %s", hipGetErrorString(e)); break; }
     }
-    // the staging buffer is the caller's again only once every DMA that reads it is done
     for (int i = 0; i < made; ++i) {
-        if (result == GEMM_OK && i < nchunks) {
+        // synchronous form: the staging buffer is the caller's again only once every DMA that
+        // reads it is done; the asynchronous form leaves the last ones running (an event may be
+        // destroyed while its work is pending)
+        if ((drain || result != GEMM_OK) && i < nchunks) {
             const hipError_t e = hipEventSynchronize(ev[i]);
-            if (e != hipSuccess) result = fail(GEMM_ERR_HIP, "staged copy failed: %s", hipGetErrorString(e));
+            if (e != hipSuccess && result == GEMM_OK) result = fail(GEMM_ERR_HIP, "staged copy failed: %s", hipGetErrorString(e));
         }
         (void)hipEventDestroy(ev[i]);
     }
     return result;
+}
+
+}  // namespace
+
+extern "C" {
+
+gemm_status_t gemm_h2d_staged(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
+                              int nstage, hipStream_t stream) {
+    return h2d_ring(dst, src, bytes, staging, chunk_bytes, nstage, stream, true);
+}
+
+gemm_status_t gemm_h2d_staged_async(void* dst, const void* src, int64_t bytes, void* staging, int64_t chunk_bytes,
+                                    int nstage, hipStream_t stream) {
+    return h2d_ring(dst, src, bytes, staging, chunk_bytes, nstage, stream, false);
 }
 
 const char* gemm_status_string(gemm_status_t s) {

@@ -34,7 +34,8 @@ KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
            "gemm_bf16_ws", "gemm_f16_ws", "gemm_ws_static", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_tune_ws",
-           "gemm_schedule", "gemm_pipe_copy", "gemm_h2d_staged", "gemm_status_string", "gemm_last_error")
+           "gemm_schedule", "gemm_pipe_copy", "gemm_h2d_staged", "gemm_h2d_staged_async", "gemm_status_string",
+           "gemm_last_error")
 
 
 class GemmOpts(ctypes.Structure):
@@ -106,8 +107,9 @@ def load():
         lib.gemm_tune_ws.restype = i32
         lib.gemm_pipe_copy.argtypes = [vp, vp, i64, i32, vp]
         lib.gemm_pipe_copy.restype = i32
-        lib.gemm_h2d_staged.argtypes = [vp, vp, i64, vp, i64, i32, vp]
-        lib.gemm_h2d_staged.restype = i32
+        for name in ("gemm_h2d_staged", "gemm_h2d_staged_async"):
+            getattr(lib, name).argtypes = [vp, vp, i64, vp, i64, i32, vp]
+            getattr(lib, name).restype = i32
         lib.gemm_status_string.argtypes = [i32]
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_last_error.argtypes = []
@@ -226,6 +228,12 @@ def gemm_h2d_staged(dst: int, src: int, nbytes: int, staging: int, chunk_bytes: 
                     stream: int = 0) -> int:
     """dst (device) = src (pageable host) through nstage page-locked staging slots."""
     return load().gemm_h2d_staged(dst, src, nbytes, staging, chunk_bytes, nstage, stream)
+
+
+def gemm_h2d_staged_async(dst: int, src: int, nbytes: int, staging: int, chunk_bytes: int, nstage: int = 2,
+                          stream: int = 0) -> int:
+    """gemm_h2d_staged returning before the last DMAs finish (sync `stream` before reusing staging)."""
+    return load().gemm_h2d_staged_async(dst, src, nbytes, staging, chunk_bytes, nstage, stream)
 
 
 def gemm_status_string(s: int) -> str:
