@@ -149,6 +149,36 @@ class Workload:
         torch.cuda.synchronize()
         return min(a.elapsed_time(b) for a, b in ev)
 
+    def vendor_call(self):
+        """A callable running the vendor library (torch's matmul, i.e. hipBLASLt / rocBLAS)
+        on this workload's operands, or None where the call has no torch equivalent (mixed
+        fp32 C with 16-bit inputs).  Context only: it writes its own output tensor."""
+        p = self.p
+        if p.beta != 0 or p.alpha != 1 or p.out != p.dtype:
+            return None
+        A = self.A.as_strided((p.M, p.K), (p.A.ld, 1) if p.A.layout == inputs.ROW else (1, p.A.ld))
+        B = self.B.as_strided((p.K, p.N), (p.B.ld, 1) if p.B.layout == inputs.ROW else (1, p.B.ld))
+        out = torch.empty((p.M, p.N), dtype=A.dtype, device=A.device)
+        # a column-major B is the transposed view of a row-major (N, K) matrix, the
+        # nn.Linear weight layout; the library call takes it as a transposed operand
+        return lambda: torch.mm(A, B, out=out)
+
+    def time_vendor(self, steps: int, warmup: int):
+        f = self.vendor_call()
+        if f is None:
+            return None
+        for _ in range(warmup):
+            f()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(self.stream)
+        for _ in range(steps):
+            f()
+        e1.record(self.stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
     def compulsory_bytes(self):
         """A and B read once, C written once (and read once when beta != 0)."""
         p = self.p
@@ -406,6 +436,9 @@ def main():
     ap.add_argument("--full-oracle", action="store_true",
                     help="check every element of the bf16 8192^3 and f16 MLP results against the oracle "
                          "(about a minute of host time) instead of a row sample")
+    ap.add_argument("--vendor", action="store_true",
+                    help="with --only: time the vendor BLAS (torch.mm) on the workload instead of this "
+                         "library (for profiling the vendor kernel beside ours)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy kernel of this many MiB "
                          "(read + write) a few times: the reference for scaling HBM counters")
@@ -466,6 +499,14 @@ def main():
                             % args.config, "clock_adjusted_peak": round(PEAK[dt] * ghz / 2.4, 1),
                             "frac_of_clock_adjusted_peak": round(value / (PEAK[dt] * ghz / 2.4), 4)}
 
+    if args.only and args.vendor:
+        ms = w.time_vendor(args.steps, args.warmup)
+        if ms is None:
+            print(f"no vendor call for {args.config}", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps({"vendor": WORKLOAD_NAME[args.config], "ms": round(ms, 5),
+                          "tflops": round(w.flops / (ms * 1e-3) / 1e12, 2)}), flush=True)
+        return
     if args.only:
         headline()
         print(json.dumps(rec), flush=True)
@@ -492,6 +533,15 @@ def main():
             entry["frac_of_peak"] = round(entry["tflops"] / PEAK[ww.p.dtype], 4)
             tmin = ww.time_min(min(reps, 30))
             entry["ms_min"] = round(tmin, 5)
+            # context: the vendor library on the same operands in the same run, then this
+            # library's default call again right after it (same clock state)
+            tv = ww.time_vendor(reps, 5) if name != "c1" else None
+            if tv is not None:
+                t2 = ww.time(reps, 5)
+                entry["vendor_context"] = {"what": "torch.mm (the vendor BLAS) on the same operands, same stream",
+                                           "ms": round(tv, 5), "tflops": round(ww.flops / (tv * 1e-3) / 1e12, 2),
+                                           "ours_right_after_ms": round(t2, 5),
+                                           "ours_right_after_tflops": round(ww.flops / (t2 * 1e-3) / 1e12, 2)}
             entry["compulsory_hbm_GB/s"] = round(ww.compulsory_bytes() / (t * 1e-3) / 1e9, 1)
             # pipelining comparison on the ring kernel of the default tile
             if pl.kernel in (lg.GEMM_KERNEL_VALU_RING, lg.GEMM_KERNEL_MFMA_RING):
