@@ -52,6 +52,13 @@
  *   GEMM_ERR_HIP -- the HIP runtime refused the launch (message in gemm_last_error()).
  *   Quick returns (BLAS): M == 0 or N == 0 -> OK, nothing launched.  K == 0 or
  *   alpha == 0 -> C = beta*C (beta == 0 writes zeros without reading C).
+ *
+ * Debugging: with GEMM_DEBUG set to anything but "" or "0" in the environment (read
+ *   once, at the first planning call), every kernel choice is printed to stderr -- the
+ *   problem, the kernel family / tile / stage count / grid / LDS picked and, when the
+ *   automatic choice passed over the direct global->LDS ring, why -- as is every
+ *   non-OK status and every operand rewrite of the workspace path.  Planning probes
+ *   (gemm_workspace_size, the tuner, the workspace path's first try) print too.
  */
 #ifndef LIBGEMM_H
 #define LIBGEMM_H

@@ -425,3 +425,28 @@ def test_static_workspace_entry_rejects_before_touching_the_device():
     s, n, _ = ws_size(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, lda=2049, beta=1.0,
                       kernel=lg.GEMM_KERNEL_MFMA_RING, tile=29)
     assert s == 0 and 0 < n <= lg.GEMM_STATIC_WS_BYTES
+
+
+def test_debug_env_prints_every_choice_and_error():
+    """GEMM_DEBUG=1: each plan is described on stderr (kernel, tile, stage count, why the
+    direct ring was passed over), and so is a refused call; without it, nothing is printed."""
+    import subprocess
+    import sys
+    code = (
+        "import sys; sys.path.insert(0, %r)\n"
+        "from tiled_stage_software_amd import libgemm as lg\n"
+        "lg.gemm_plan(1, 1, 0, 1, 8192, 8192, 8192, 1.0, 16, 8192, 16, 8192, 0.0, 16, 8192, None)\n"
+        "lg.gemm_plan(1, 1, 1, 1, 512, 512, 512, 1.0, 16, 512, 16, 512, 0.0, 16, 512, None)\n"
+        "lg.gemm_plan(0, 0, 0, 0, 64, 64, 64, 1.0, 16, 64, 16, 64, 0.0, 16, 64, lg.GemmOpts(9, 0, 0, 0))\n"
+    ) % ROOT
+    env = dict(os.environ, GEMM_DEBUG="1")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0, r.stderr
+    lines = [l for l in r.stderr.splitlines() if l.startswith("libgemm:")]
+    assert any("M=8192 N=8192 K=8192" in l and "-> mfma_ring tile 24" in l and "nstage 2" in l for l in lines), lines
+    assert any("-> mfma_staged" in l and "direct ring passed over: needs A row-major and B column-major" in l
+               for l in lines), lines
+    assert any("status 2" in l and "nstage 9" in l for l in lines), lines
+    env.pop("GEMM_DEBUG")
+    r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert r.returncode == 0 and "libgemm:" not in r.stderr

@@ -6,6 +6,7 @@
 // caller's stream without synchronising.
 #include <stdarg.h>
 #include <stdio.h>
+#include <stdlib.h>
 #include <string.h>
 
 #include <vector>
@@ -20,11 +21,14 @@ using gemm::GemmParams;
 
 thread_local char g_err[512] = "";
 
+bool debug_on();
+
 gemm_status_t fail(gemm_status_t s, const char* fmt, ...) {
     va_list ap;
     va_start(ap, fmt);
     vsnprintf(g_err, sizeof(g_err), fmt, ap);
     va_end(ap);
+    if (debug_on()) fprintf(stderr, "libgemm: status %d: %s\n", (int)s, g_err);
     return s;
 }
 
@@ -151,6 +155,44 @@ gemm_status_t validate(const Problem& q) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// GEMM_DEBUG=1 in the environment: every kernel choice is described on stderr (read once;
+// the static's initialisation is thread-safe and it never changes afterwards).
+bool debug_on() {
+    static const bool on = [] {
+        const char* e = getenv("GEMM_DEBUG");
+        return e != nullptr && e[0] != 0 && !(e[0] == '0' && e[1] == 0);
+    }();
+    return on;
+}
+
+const char* kernel_name(int k) {
+    switch (k) {
+        case GEMM_KERNEL_VALU_RING: return "valu_ring";
+        case GEMM_KERNEL_VALU_STAGED: return "valu_staged";
+        case GEMM_KERNEL_MFMA_RING: return "mfma_ring";
+        case GEMM_KERNEL_MFMA_STAGED: return "mfma_staged";
+        case GEMM_KERNEL_SCALE: return "scale";
+        default: return "none";
+    }
+}
+
+const char* type_name(int t) { return t == gemm::DT_F32 ? "f32" : t == gemm::DT_BF16 ? "bf16" : "f16"; }
+
+// One line per decision: the problem, what was picked and, when the direct ring was
+// passed over, why.
+void debug_plan(const Problem& q, const gemm_opts_t& o, const gemm_plan_t& pl, const char* why) {
+    if (!debug_on()) return;
+    char note[160] = "";
+    if (why && why[0]) snprintf(note, sizeof(note), " (direct ring passed over: %s)", why);
+    fprintf(stderr,
+            "libgemm: %s->%s M=%lld N=%lld K=%lld A=%s B=%s lda=%lld ldb=%lld alpha=%g beta=%g "
+            "opts(kernel=%d tile=%d nstage=%d flags=0x%x) -> %s tile %d %dx%dx%d nstage %d grid %lld lds %d%s\n",
+            type_name(q.in_type), type_name(q.c_type), (long long)q.M, (long long)q.N, (long long)q.K,
+            q.la == GEMM_ROW_MAJOR ? "row" : "col", q.lb == GEMM_ROW_MAJOR ? "row" : "col", (long long)q.lda,
+            (long long)q.ldb, q.alpha, q.beta, o.kernel, o.tile, o.nstage, o.flags, kernel_name(pl.kernel), pl.tile,
+            pl.bm, pl.bn, pl.bk, pl.nstage, (long long)pl.grid, pl.lds_bytes, note);
+}
+
 // LDS a kernel of this tile allocates statically: the ring, or for the split-copy tiles
 // with 256 columns and a 16-bit C, at least the C tile (bm x 256 x 2 bytes), which their
 // epilogue stages through LDS after the K loop whatever the stage count.
@@ -245,6 +287,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
 
     if (q.M == 0 || q.N == 0) {
         plan->kernel = GEMM_KERNEL_AUTO;
+        debug_plan(q, opts, *plan, "");
         return GEMM_OK;  // nothing to do, nothing launched
     }
     if (q.K == 0 || q.alpha == 0.0f || opts.kernel == GEMM_KERNEL_SCALE) {
@@ -256,6 +299,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
         plan->threads = 256;
         int64_t blocks = cdiv(q.M * q.N, 256);
         plan->grid = blocks > 65536 ? 65536 : blocks;
+        debug_plan(q, opts, *plan, "");
         return GEMM_OK;
     }
 
@@ -350,6 +394,8 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     gp->tiles_n = (int)cdiv(q.N, t->bn);
     plan->grid = (int64_t)gp->tiles_m * gp->tiles_n;
     if (plan->grid > INT32_MAX) return fail(GEMM_ERR_UNSUPPORTED, "too many tiles");
+    const bool passed_over = opts.kernel == 0 && (kernel == GEMM_KERNEL_VALU_STAGED || kernel == GEMM_KERNEL_MFMA_STAGED);
+    debug_plan(q, opts, *plan, passed_over ? why : "");
     return GEMM_OK;
 }
 
@@ -452,7 +498,15 @@ gemm_status_t run_ws(const Problem& q, const gemm_opts_t* opts, void* ws, size_t
     s = plan_ws(q, opts, ws, &pp, &plan, &gp);
     if (s != GEMM_OK) return s;
     if (!(pp.a || pp.b)) return launch(q.in_type, plan, gp, stream);
-    if (!ws || (int64_t)ws_bytes < pp.a_bytes + pp.b_bytes) return run(q, opts, stream);  // too small: as gemm_*_ex
+    if (!ws || (int64_t)ws_bytes < pp.a_bytes + pp.b_bytes) {
+        if (debug_on())
+            fprintf(stderr, "libgemm: workspace of %zu bytes < the %lld the rewrite needs: the plain call\n", ws_bytes,
+                    (long long)(pp.a_bytes + pp.b_bytes));
+        return run(q, opts, stream);  // too small: as gemm_*_ex
+    }
+    if (debug_on())
+        fprintf(stderr, "libgemm: workspace path rewrites%s%s K-contiguous, K' = %lld, then the ring above\n",
+                pp.a ? " A" : "", pp.b ? " B" : "", (long long)pp.kp);
     gemm::PackParams pk;
     memset(&pk, 0, sizeof(pk));
     char* base = static_cast<char*>(ws);
