@@ -111,6 +111,16 @@ typedef struct gemm_opts {
  * nStage variants run at the same occupancy (the fair comparison: at natural occupancy a
  * shallower ring leaves room for more resident workgroups).  Results are unchanged. */
 #define GEMM_FLAG_EQUAL_LDS 2
+/* Debugging: the LDS-poisoning variant of the ring kernel.  Right after the barrier that
+ * releases a ring slot (all its reads done, nothing yet copied into it) the workgroup
+ * overwrites the slot with all-ones bits (NaN in bf16, f16 and fp32) and meets at a second
+ * barrier before the next copy into it is issued, so a pipeline that read a slot outside
+ * its live range would produce NaN instead of a plausible stale value.  Built for the
+ * default tiles only -- fp32 ring tile 5 (nstage 1-4), bf16 ring tiles 24 and 30 (nstage
+ * 1, 2) -- and not for the kernels that run on rewritten operands in the workspace path;
+ * any other plan with this flag is GEMM_ERR_UNSUPPORTED.  Results are unchanged; the
+ * extra stores and barrier per slab make it slower. */
+#define GEMM_FLAG_POISON_LDS 4
 
 /* What a call would launch (filled by gemm_plan; no GPU needed). */
 typedef struct gemm_plan {

@@ -73,7 +73,7 @@ F32, BF16, F16 = lg.GEMM_F32, lg.GEMM_BF16, lg.GEMM_F16
     (dict(la=7), lg.GEMM_ERR_INVALID_ARG),
     (dict(nstage=6), lg.GEMM_ERR_UNSUPPORTED),
     (dict(nstage=-1), lg.GEMM_ERR_UNSUPPORTED),
-    (dict(flags=4), lg.GEMM_ERR_INVALID_ARG),
+    (dict(flags=8), lg.GEMM_ERR_INVALID_ARG),
     (dict(kernel=lg.GEMM_KERNEL_MFMA_RING), lg.GEMM_ERR_UNSUPPORTED),   # fp32 input on the MFMA path
     (dict(kernel=lg.GEMM_KERNEL_VALU_RING, A=A16 + 4), lg.GEMM_ERR_UNSUPPORTED),  # misaligned
     (dict(kernel=lg.GEMM_KERNEL_VALU_STAGED, nstage=3), lg.GEMM_ERR_UNSUPPORTED),
@@ -450,3 +450,20 @@ def test_debug_env_prints_every_choice_and_error():
     env.pop("GEMM_DEBUG")
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0 and "libgemm:" not in r.stderr
+
+
+def test_poison_flag_is_planned_only_where_its_variant_is_built():
+    """GEMM_FLAG_POISON_LDS: the default fp32 ring tile and the bf16 tiles 24 / 30 plan with
+    it; anything else is refused before a launch."""
+    P = lg.GEMM_FLAG_POISON_LDS
+    s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, flags=P)
+    assert s == 0 and p.tile == 24
+    s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0, lda=2049, flags=P)
+    assert s == 0 and p.tile == 30
+    s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, flags=P)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and p.tile == 5
+    for S in (1, 2, 3, 4):
+        assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, flags=P)[0] == 0
+    assert plan(F16, F16, ROW, COL, 8192, 8192, 8192, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED   # not built for f16
+    assert plan(F32, F32, ROW, ROW, 256, 256, 256, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED      # small tile 7
+    assert plan(BF16, BF16, COL, COL, 512, 512, 512, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # staged kernel

@@ -532,3 +532,35 @@ def test_row_major_ring_exact_on_tails_and_pitches(case):
     bits = torch.int32 if out == "f32" else torch.int16
     assert torch.equal(a.view(bits), b.view(bits))
     assert err_vs_oracle(q, a) <= TOL[dtype]
+
+
+# --------------------------------------------------------------- LDS-poisoning variants
+
+POISON_CASES = [  # (dtype, out, la, lb, kernel, tile, stages, M, N, K, alpha, beta): several slabs, ragged M / N
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 5, (1, 2, 3, 4), 300, 200, 160, 1.0, 0.0),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, (1, 2), 520, 600, 448, 1.0, 0.0),
+    ("bf16", "f32", ROW, COL, K_MFMA_RING, 24, (1, 2), 300, 264, 320, 0.5, 1.0),
+    ("bf16", "f32", ROW, ROW, K_MFMA_RING, 30, (1, 2), 400, 520, 449, 0.5, 1.0),
+    ("bf16", "bf16", ROW, ROW, K_MFMA_RING, 30, (1, 2), 197, 256, 130, 1.0, 0.0),
+]
+
+
+@pytest.mark.parametrize("case", POISON_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}-{'RC'[c[2]]}{'RC'[c[3]]}-t{c[5]}-{c[7]}x{c[8]}x{c[9]}")
+def test_poisoned_ring_changes_no_bit(case):
+    """With every ring slot overwritten by NaN bits as soon as it is released, the default
+    ring kernels give the same bits as without it, exact on small integers and on all-ones
+    operands (where a stale slab would be indistinguishable from the right one and only the
+    poison could show a read outside a slot's live range)."""
+    dtype, out, la, lb, kern, tile, stages, M, N, K, alpha, beta = case
+    for dist in ("int2", "ones"):
+        p = problem(dtype, out, M, N, K, la, lb, dist=dist, alpha=alpha, beta=beta, seed=83)
+        want = expected_rounded(oracle_ref(p), p.out)
+        for S in stages:
+            say(f"[poison] {dtype}->{out} tile={tile} S={S} {M}x{N}x{K} {dist}")
+            got = run(p, kernel=kern, tile=tile, nstage=S, flags=lg.GEMM_FLAG_POISON_LDS)
+            plain = run(p, kernel=kern, tile=tile, nstage=S)
+            assert not torch.isnan(got.float()).any()
+            assert np.array_equal(got.double().numpy(), want)
+            assert torch.equal(got.contiguous().view(torch.int16 if out != "f32" else torch.int32),
+                               plain.contiguous().view(torch.int16 if out != "f32" else torch.int32))

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "schedule.hpp"
 
 namespace gemm {
@@ -35,6 +37,7 @@ struct GemmParams {
     int xcd_remap;          // 1 = spread consecutive tiles onto one XCD
     int a_vec, b_vec;       // staged kernels: 16-byte vector loads are legal for A / B
     int lds_pad;            // host only: extra dynamic LDS bytes per workgroup (equal-occupancy runs)
+    int poison;             // host only: 1 = launch the LDS-poisoning debug variant of the kernel
 };
 
 // ---------------------------------------------------------------- waits and barriers
@@ -55,6 +58,28 @@ __device__ __forceinline__ void wait_lgkm0() { asm volatile("s_waitcnt lgkmcnt(0
 // "memory" so that the compiler moves no LDS access across it; the hardware ordering
 // (this wave's own LDS / copy traffic completed) is the explicit s_waitcnt before it.
 __device__ __forceinline__ void barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+// Debugging wrapper of a ring kernel's K-loop operations.  Right after the barrier that
+// releases a ring slot (every wave has finished reading the slab in it; nothing has been
+// copied into it yet) each thread of the workgroup overwrites its share of the slot with
+// all-ones bits -- NaN as bf16, f16 and fp32 -- waits for its writes, and meets the others
+// at a second barrier before anything can be issued into the slot.  A fragment read of a
+// released slot, or one that runs ahead of the copy it should wait for, then reads NaN
+// instead of a stale slab, and the result shows it whatever the inputs (all-ones or
+// identity operands included).  The protocol calls release() through the K-loop template's
+// hook; kernels built without this wrapper contain no trace of it.
+template <class Base>
+struct PoisonOps : Base {
+    __device__ __forceinline__ void release(int slot) {
+        LDS_AS char* st = this->smem + slot * Base::STAGE;
+        for (int i = (int)threadIdx.x * 16; i < Base::STAGE; i += (int)blockDim.x * 16)
+            *reinterpret_cast<LDS_AS u32x4*>(st + i) = u32x4{~0u, ~0u, ~0u, ~0u};
+        wait_lgkm0();
+        barrier();
+    }
+};
+template <bool POISON, class O>
+using MaybePoison = typename std::conditional<POISON, PoisonOps<O>, O>::type;
 
 // Waves per SIMD that the LDS footprint allows (4 SIMDs per CU, 160 KiB of LDS),
 // clamped to [1, cap]; used as the kernels' amdgpu_waves_per_eu so that the compiler

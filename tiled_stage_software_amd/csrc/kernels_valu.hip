@@ -165,12 +165,12 @@ struct ValuRingOps : ValuCompute<BM, BN, BK, TM, TN, KW> {
     __device__ __forceinline__ void math(int) { C::template math<BUF>(); }
 };
 
-template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
+template <int BM, int BN, int BK, int TM, int TN, int S, int KW, bool POISON>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) __attribute__((amdgpu_waves_per_eu(
     occupancy_waves((BM / TM) * (BN / TN), S * ValuCompute<BM, BN, BK, TM, TN>::STAGE,
                     TM * TN >= 64 ? (KW == 4 ? 2 : 3) : (TM * TN >= 32 ? 3 : 4)))))
 void valu_ring_kernel(const GemmParams p) {
-    typedef ValuRingOps<BM, BN, BK, TM, TN, S, KW> Ops;
+    typedef MaybePoison<POISON, ValuRingOps<BM, BN, BK, TM, TN, S, KW>> Ops;
     __shared__ __attribute__((aligned(1024))) char smem_raw[S * Ops::STAGE];
     int tm, tn;
     tile_coords(p, tm, tn);
@@ -233,7 +233,14 @@ void valu_staged_kernel(const GemmParams p) {
 // ---------------------------------------------------------------- launch tables
 template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
 static hipError_t launch_ring(const GemmParams& p, hipStream_t st) {
-    hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S, KW>), dim3(p.tiles_m * p.tiles_n),
+    hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S, KW, false>), dim3(p.tiles_m * p.tiles_n),
+                       dim3((BM / TM) * (BN / TN)), p.lds_pad, st, p);
+    return hipGetLastError();
+}
+// The LDS-poisoning debug variant (built for the default fp32 tile only).
+template <int BM, int BN, int BK, int TM, int TN, int S, int KW>
+static hipError_t launch_ring_poison(const GemmParams& p, hipStream_t st) {
+    hipLaunchKernelGGL((valu_ring_kernel<BM, BN, BK, TM, TN, S, KW, true>), dim3(p.tiles_m * p.tiles_n),
                        dim3((BM / TM) * (BN / TN)), p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -260,6 +267,15 @@ static hipError_t ring_stages(int S, const GemmParams& p, hipStream_t st) {
 }
 
 hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream_t st) {
+    if (p.poison && tile == 5) {
+        switch (nstage) {
+            case 1: return launch_ring_poison<128, 64, 16, 8, 4, 1, 4>(p, st);
+            case 2: return launch_ring_poison<128, 64, 16, 8, 4, 2, 4>(p, st);
+            case 3: return launch_ring_poison<128, 64, 16, 8, 4, 3, 4>(p, st);
+            case 4: return launch_ring_poison<128, 64, 16, 8, 4, 4, 4>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (tile) {
         case 1: return ring_stages<128, 64, 16, 8, 8, 2>(nstage, p, st);  // 128 threads, 2-k steps (8-byte A reads)
         case 2: return ring_stages<64, 64, 16, 4, 4>(nstage, p, st);   // 256 threads

@@ -255,7 +255,7 @@ bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
 gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, GemmParams* gp) {
     gemm_opts_t opts = {0, 0, 0, 0};
     if (o) opts = *o;
-    if (opts.flags & ~(GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_EQUAL_LDS))
+    if (opts.flags & ~(GEMM_FLAG_NO_XCD_REMAP | GEMM_FLAG_EQUAL_LDS | GEMM_FLAG_POISON_LDS))
         return fail(GEMM_ERR_INVALID_ARG, "unknown flags 0x%x", opts.flags);
     if (opts.nstage < 0 || opts.nstage > GEMM_MAX_NSTAGE) return fail(GEMM_ERR_UNSUPPORTED, "nstage %d out of range", opts.nstage);
     if (opts.kernel < 0 || opts.kernel > GEMM_KERNEL_SCALE) return fail(GEMM_ERR_INVALID_ARG, "kernel %d unknown", opts.kernel);
@@ -389,6 +389,15 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
             if ((t->stages & (1 << d)) && static_lds(*t, d, kernel, q.c_type) <= kLdsLimit) { deepest = d; break; }
         gp->lds_pad = static_lds(*t, deepest, kernel, q.c_type) - lds;
         plan->lds_bytes += gp->lds_pad;
+    }
+    if (opts.flags & GEMM_FLAG_POISON_LDS) {
+        // the debugging variant exists for the default tiles only (the launch tables)
+        const bool built = (kernel == GEMM_KERNEL_VALU_RING && t->id == 5) ||
+                           (kernel == GEMM_KERNEL_MFMA_RING && q.in_type == gemm::DT_BF16 && (t->id == 24 || t->id == 30));
+        if (!built)
+            return fail(GEMM_ERR_UNSUPPORTED, "no LDS-poisoning build of kernel %d tile %d for this input type", kernel,
+                        t->id);
+        gp->poison = 1;
     }
     gp->tiles_m = (int)cdiv(q.M, t->bm);
     gp->tiles_n = (int)cdiv(q.N, t->bn);

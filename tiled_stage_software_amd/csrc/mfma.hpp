@@ -442,7 +442,7 @@ struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
     __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (L + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD, bool POISON>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_split_kernel(const GemmParams p) {
     static constexpr int STAGE = (BM + BN) * BK * 2;
@@ -464,7 +464,7 @@ void mfma_split_kernel(const GemmParams p) {
     const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
                          n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
     if (wave_id() < NC) {
-        SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true> ops;
+        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true>> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
@@ -474,7 +474,7 @@ void mfma_split_kernel(const GemmParams p) {
         }
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     } else {
-        SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false> ops;
+        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false>> ops;
         ops.init((LDS_AS char*)(smem_raw));
         gemm_sched::ring_mainloop<S, BK / 16, SPREAD ? BK / 16 : 0>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
@@ -577,10 +577,11 @@ static hipError_t launch_splitp(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false,
+          bool POISON = false>
 static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD>), dim3(grid), dim3(WM * WN * 64),
+    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD, POISON>), dim3(grid), dim3(WM * WN * 64),
                        p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -696,7 +697,7 @@ struct KnSplitOps : MfmaKnCompute<T, BM, BN, BK, WM, WN> {
     __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (LB + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool POISON>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_kn_kernel(const GemmParams p) {
     static_assert(S == 1 || S == 2, "the staged half of the protocol holds one slab in registers");
@@ -718,7 +719,7 @@ void mfma_kn_kernel(const GemmParams p) {
                          n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
     constexpr int KS = BK / 16;
     if (wave_id() < NC) {
-        KnSplitOps<T, BM, BN, BK, WM, WN, NC, true> ops;
+        MaybePoison<POISON, KnSplitOps<T, BM, BN, BK, WM, WN, NC, true>> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.numK = numK;
         ops.k_last = k_last;
@@ -730,7 +731,7 @@ void mfma_kn_kernel(const GemmParams p) {
         }
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     } else {
-        KnSplitOps<T, BM, BN, BK, WM, WN, NC, false> ops;
+        MaybePoison<POISON, KnSplitOps<T, BM, BN, BK, WM, WN, NC, false>> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.numK = numK;
         gemm_sched::ring_mainloop<S, KS, S == 1 ? 0 : KS>(ops, numK);
@@ -741,10 +742,10 @@ void mfma_kn_kernel(const GemmParams p) {
     }
 }
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool POISON = false>
 static hipError_t launch_kn(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_kn_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC>), dim3(grid), dim3(WM * WN * 64),
+    hipLaunchKernelGGL((mfma_kn_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, POISON>), dim3(grid), dim3(WM * WN * 64),
                        p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -1010,6 +1011,10 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             break;
         case 24:  // tile 23 with each slab's copies spread over the k-steps (S = 1: one slot,
                   // the slab's copies go out together, as in tile 23)
+            if constexpr (std::is_same<T, __bf16>::value) {   // the LDS-poisoning debug variant
+                if (p.poison && S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, true>(p, st);
+                if (p.poison && S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, true>(p, st);
+            }
             if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true>(p, st);
             if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true>(p, st);
             break;
@@ -1025,6 +1030,10 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             if (S == 2) return launch_splitp<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
             break;
         case 30:  // 192x256x64, 2x4 waves of 96x64: row-major A through registers, row-major B in place
+            if constexpr (std::is_same<T, __bf16>::value) {   // the LDS-poisoning debug variant
+                if (p.poison && S == 1) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 1, 4, true>(p, st);
+                if (p.poison && S == 2) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 2, 4, true>(p, st);
+            }
             if (S == 1) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
             break;

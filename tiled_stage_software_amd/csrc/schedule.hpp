@@ -48,6 +48,15 @@ GEMM_HD constexpr int imax(int a, int b) { return a > b ? a : b; }
 
 enum { BODY_MAIN = 0, BODY_MAIN_END = 1, BODY_TAIL = 2, BODY_LAST = 3 };
 
+// Hook right after the barrier that releases a ring slot: every wave has finished reading
+// the slab in it and nothing has been issued into it yet.  Ops without a release member
+// (the production kernels) do nothing there; the LDS-poisoning debug wrapper overwrites
+// the slot.
+template <class O>
+GEMM_HD auto release_(O& o, int slot, int) -> decltype(o.release(slot), void()) { o.release(slot); }
+template <class O>
+GEMM_HD void release_(O&, int, long) {}
+
 // One slab of KS k-steps.  Every branch here is on compile-time values, so the unrolled
 // body is straight-line code (a run-time branch inside it lets the compiler sink the
 // math below it and keep every fragment of the slab live at once).
@@ -79,6 +88,7 @@ GEMM_HD void ring_slab(Ops& ops, int kt, int slot, int issue_slot, int next_slot
                 ops.wait_lds();
                 ops.template wait_slabs<BODY == BODY_TAIL ? 0 : S - 2>();
                 ops.barrier();
+                release_(ops, slot, 0);
                 ops.template frag<0>(kt + 1, next_slot, 0);
                 // the barrier freed this slab's slot: start the copy of slab kt+S into it
                 if (PARTS > 0 && BODY == BODY_MAIN) { ops.issue(kt + S, slot, 0, PARTS); copies_here = PARTS == 1 ? KS : 1; }
@@ -138,6 +148,7 @@ GEMM_HD void ring_mainloop(Ops& ops, int numK) {
             single_slab_compute<KS>(ops, kt);
             ops.wait_lds();
             ops.barrier();
+            release_(ops, 0, 0);
             after_slab_(ops, kt, 0);
         }
     } else {

@@ -26,6 +26,7 @@ GEMM_F32, GEMM_BF16, GEMM_F16 = 0, 1, 2
  GEMM_KERNEL_MFMA_STAGED, GEMM_KERNEL_SCALE) = range(6)
 GEMM_FLAG_NO_XCD_REMAP = 1
 GEMM_FLAG_EQUAL_LDS = 2
+GEMM_FLAG_POISON_LDS = 4
 GEMM_MAX_NSTAGE = 4
 GEMM_STATIC_WS_BYTES = 33554432
 
