@@ -125,7 +125,7 @@ def test_plans_for_the_workloads():
     # bf16 8192^3 NT -> MFMA ring, 256x256 split-copy tile (8 waves), two slots
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and (p.bm, p.bn, p.bk) == (256, 256, 64)
-    assert p.tile == 24 and p.threads == 512 and p.nstage == 2 and p.grid == 32 * 32 and p.lds_bytes <= 163840
+    assert p.tile == 31 and p.threads == 512 and p.nstage == 2 and p.grid == 32 * 32 and p.lds_bytes <= 163840
     # f16 MLP shape NT
     s, p = plan(F16, F16, ROW, COL, 16384, 14336, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and p.grid == 64 * 56
@@ -443,7 +443,7 @@ def test_debug_env_prints_every_choice_and_error():
     r = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
     assert r.returncode == 0, r.stderr
     lines = [l for l in r.stderr.splitlines() if l.startswith("libgemm:")]
-    assert any("M=8192 N=8192 K=8192" in l and "-> mfma_ring tile 24" in l and "nstage 2" in l for l in lines), lines
+    assert any("M=8192 N=8192 K=8192" in l and "-> mfma_ring tile 31" in l and "nstage 2" in l for l in lines), lines
     assert any("-> mfma_staged" in l and "direct ring passed over: needs A row-major and B column-major" in l
                for l in lines), lines
     assert any("status 2" in l and "nstage 9" in l for l in lines), lines
@@ -453,11 +453,13 @@ def test_debug_env_prints_every_choice_and_error():
 
 
 def test_poison_flag_is_planned_only_where_its_variant_is_built():
-    """GEMM_FLAG_POISON_LDS: the default fp32 ring tile and the bf16 tiles 24 / 30 plan with
+    """GEMM_FLAG_POISON_LDS: the default fp32 ring tile and the bf16 tiles 31 / 30 plan with
     it; anything else is refused before a launch."""
     P = lg.GEMM_FLAG_POISON_LDS
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, flags=P)
-    assert s == 0 and p.tile == 24
+    assert s == 0 and p.tile == 31
+    assert plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, kernel=lg.GEMM_KERNEL_MFMA_RING, tile=24,
+                flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED                                       # not the default tile
     s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0, lda=2049, flags=P)
     assert s == 0 and p.tile == 30
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, flags=P)

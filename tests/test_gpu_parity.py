@@ -64,6 +64,9 @@ FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= 
     ("f16", "f16", ROW, COL, K_MFMA_RING, 3, 2, 256, 384, 128),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 2, 4, 256, 512, 256),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, 2, 512, 256, 256),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 31, 2, 512, 256, 256),
+    ("f16", "f32", ROW, COL, K_MFMA_RING, 31, 1, 256, 512, 256),
+    ("bf16", "f32", ROW, COL, K_MFMA_RING, 32, 2, 384, 256, 256),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 26, 2, 256, 512, 256),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 25, 4, 256, 256, 256),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 29, 1, 384, 256, 256),
@@ -198,8 +201,8 @@ def test_full_size_small_integers_bit_exact(name):
 
 FULL_STAGES = [  # (workload, kernel family, tile, stage counts): the default tiles at full size
     ("c2", K_VALU_RING, 5, [1, 2, 3, 4]),
-    ("c3", K_MFMA_RING, 24, [1, 2]),
-    ("c4", K_MFMA_RING, 24, [1, 2]),
+    ("c3", K_MFMA_RING, 31, [1, 2]),
+    ("c4", K_MFMA_RING, 31, [1, 2]),
     ("c5", K_MFMA_RING, 30, [1, 2]),
 ]
 
@@ -235,6 +238,8 @@ RING_STAGES = [
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 18, [1, 2, 3], 768, 640, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 23, [1, 2], 768, 512, 576),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, [1, 2], 768, 512, 576),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 31, [1, 2], 768, 512, 576),
+    ("f16", "f16", ROW, COL, K_MFMA_RING, 32, [1, 2], 576, 768, 448),
     ("f16", "f32", ROW, COL, K_MFMA_RING, 29, [1, 2], 600, 768, 448),
     ("f16", "f16", ROW, COL, K_MFMA_RING, 23, [1, 2], 512, 768, 448),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 26, [1, 2], 768, 600, 576),
@@ -473,7 +478,7 @@ def test_equal_lds_padding_changes_no_bit(case):
         assert torch.equal(a, b)
 
 
-RAGGED_TILES = [(23, 2), (24, 2), (24, 1), (18, 3), (18, 1), (25, 3), (26, 2), (26, 1), (29, 1), (29, 2), (1, 2), (2, 4)]
+RAGGED_TILES = [(23, 2), (24, 2), (24, 1), (31, 2), (31, 1), (32, 2), (18, 3), (18, 1), (25, 3), (26, 2), (26, 1), (29, 1), (29, 2), (1, 2), (2, 4)]
 
 
 @pytest.mark.parametrize("ts", RAGGED_TILES, ids=lambda t: f"t{t[0]}-s{t[1]}")
@@ -538,8 +543,8 @@ def test_row_major_ring_exact_on_tails_and_pitches(case):
 
 POISON_CASES = [  # (dtype, out, la, lb, kernel, tile, stages, M, N, K, alpha, beta): several slabs, ragged M / N
     ("f32", "f32", ROW, ROW, K_VALU_RING, 5, (1, 2, 3, 4), 300, 200, 160, 1.0, 0.0),
-    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 24, (1, 2), 520, 600, 448, 1.0, 0.0),
-    ("bf16", "f32", ROW, COL, K_MFMA_RING, 24, (1, 2), 300, 264, 320, 0.5, 1.0),
+    ("bf16", "bf16", ROW, COL, K_MFMA_RING, 31, (1, 2), 520, 600, 448, 1.0, 0.0),
+    ("bf16", "f32", ROW, COL, K_MFMA_RING, 31, (1, 2), 300, 264, 320, 0.5, 1.0),
     ("bf16", "f32", ROW, ROW, K_MFMA_RING, 30, (1, 2), 400, 520, 449, 0.5, 1.0),
     ("bf16", "bf16", ROW, ROW, K_MFMA_RING, 30, (1, 2), 197, 256, 130, 1.0, 0.0),
 ]

@@ -72,6 +72,8 @@ const Tile kMfmaRing[] = {
     {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
     {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64, copies spread
     {30, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 29 on row-major A (any pitch) and row-major B
+    {31, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 24 with 16x16x32 instructions (default)
+    {32, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 29 with 16x16x32 instructions
 #ifdef GEMM_ALL_TILES  // variants that lose on every workload measured (built on request)
     {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies spread over the slab
     {5, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},     // copies spread
@@ -96,9 +98,10 @@ const Tile kMfmaRing[] = {
 // The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles (and
 // the cost model below keeps 256x256): 256x256x64, two slots, eight waves (2x4 of
 // 128x64, two per SIMD) of which one per SIMD issues the copies, each slab's copies
-// spread over its k-steps (the fastest measured on 8192^3 bf16 and on the f16 MLP shape,
-// 2% ahead of issuing them together).
-constexpr int kMfmaRingDefault = 24;
+// spread over its k-steps, 16x16x32 instructions (the fastest measured on 8192^3 bf16 and
+// on the f16 MLP shape: 2% and 4% ahead of the same tile with 32x32x16 instructions, tile
+// 24, which is itself 2% ahead of issuing each slab's copies together, tile 23).
+constexpr int kMfmaRingDefault = 31;
 
 const Tile kMfmaStaged[] = {
     {1, 128, 128, 32, 256, S1 | S2, 2, (128 + 128) * 32 * 2},
@@ -198,7 +201,8 @@ void debug_plan(const Problem& q, const gemm_opts_t& o, const gemm_plan_t& pl, c
 // epilogue stages through LDS after the K loop whatever the stage count.
 int static_lds(const Tile& t, int S, int kernel, int c_type) {
     int lds = S * t.stage_bytes;
-    const bool split = t.id == 21 || t.id == 23 || t.id == 24 || t.id == 25 || t.id == 27 || t.id == 29 || t.id == 30;
+    const bool split = t.id == 21 || t.id == 23 || t.id == 24 || t.id == 25 || t.id == 27 || t.id == 29 || t.id == 30 ||
+                       t.id == 31 || t.id == 32;
     if (kernel == GEMM_KERNEL_MFMA_RING && split && c_type != gemm::DT_F32 && t.bn == 256 && lds < t.bm * t.bn * 2)
         lds = t.bm * t.bn * 2;
     return lds;
@@ -336,7 +340,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
                 // than 256x192).
                 const int64_t cus = gemm::num_compute_units();
                 int64_t best = -1;
-                for (int id : {kMfmaRingDefault, 29, 26}) {
+                for (int id : {kMfmaRingDefault, 32, 26}) {
                     const Tile* c = find_tile(kMfmaRing, id);
                     const int64_t cost = cdiv(cdiv(q.M, c->bm) * cdiv(q.N, c->bn), cus) * c->bm * c->bn;
                     if (best < 0 || cost < best) { best = cost; big = c; }
@@ -393,7 +397,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     if (opts.flags & GEMM_FLAG_POISON_LDS) {
         // the debugging variant exists for the default tiles only (the launch tables)
         const bool built = (kernel == GEMM_KERNEL_VALU_RING && t->id == 5) ||
-                           (kernel == GEMM_KERNEL_MFMA_RING && q.in_type == gemm::DT_BF16 && (t->id == 24 || t->id == 30));
+                           (kernel == GEMM_KERNEL_MFMA_RING && q.in_type == gemm::DT_BF16 && (t->id == 31 || t->id == 30));
         if (!built)
             return fail(GEMM_ERR_UNSUPPORTED, "no LDS-poisoning build of kernel %d tile %d for this input type", kernel,
                         t->id);

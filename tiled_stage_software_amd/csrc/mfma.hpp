@@ -245,7 +245,7 @@ struct MfmaCompute {
     // instruction.  Same values as epilogue(): RNE(alpha * acc).
     template <int OUT, int NT>
     __device__ __forceinline__ void epilogue_lds(const GemmParams& p, int m0, int n0) {
-        static_assert(OUT != DT_F32 && BN == 256 && MI == 32, "16-bit rows of 256 columns");
+        static_assert(OUT != DT_F32 && BN == 256, "16-bit rows of 256 columns");
         constexpr int RB = BN * 2;   // bytes per tile row
         constexpr int CPR_C = RB / 16;
         wait_lgkm0();
@@ -417,9 +417,9 @@ void mfma_ring_kernel(const GemmParams p) {
 // one per SIMD -- issue and wait for the copies, so when one of them stalls on a copy the
 // other wave of its SIMD keeps the matrix core busy.  Both kinds run the same K-loop
 // template and meet at the same barriers.
-template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool COPY>
-struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
-    typedef MfmaCompute<T, BM, BN, BK, WM, WN, 32> C;
+template <typename T, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool COPY, int MI = 32>
+struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, MI> {
+    typedef MfmaCompute<T, BM, BN, BK, WM, WN, MI> C;
     DirectLoader<BM, C::ROWB, NC, true> la;
     DirectLoader<BN, C::ROWB, NC, true> lb;
     static constexpr int L = DirectLoader<BM, C::ROWB, NC, true>::IPW + DirectLoader<BN, C::ROWB, NC, true>::IPW;
@@ -442,9 +442,11 @@ struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
     __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (L + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD, bool POISON>
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD, bool POISON,
+          int MI>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_split_kernel(const GemmParams p) {
+    constexpr int KS = MfmaCompute<T, BM, BN, BK, WM, WN, MI>::KS;
     static constexpr int STAGE = (BM + BN) * BK * 2;
     // a 16-bit C tile of 256 columns leaves through LDS after the K loop (epilogue_lds):
     // at least that much LDS whatever the ring (one workgroup per CU either way)
@@ -464,19 +466,19 @@ void mfma_split_kernel(const GemmParams p) {
     const bool lds_epi = LDS_EPI && p.beta == 0.0f && m0 == m_keep && n0 == n_keep && m0 + BM <= p.M &&
                          n0 + BN <= p.N && (reinterpret_cast<uintptr_t>(p.C) & 15) == 0 && (p.ldc * 2) % 16 == 0;
     if (wave_id() < NC) {
-        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true>> ops;
+        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, true, MI>> ops;
         ops.init((LDS_AS char*)(smem_raw));
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-        gemm_sched::ring_mainloop<S, BK / 16, SPREAD ? BK / 16 : 0>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, KS, SPREAD ? KS : 0>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
         ops.template epilogue<OUT>(p, m0, n0, m_keep, n_keep);
     } else {
-        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false>> ops;
+        MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false, MI>> ops;
         ops.init((LDS_AS char*)(smem_raw));
-        gemm_sched::ring_mainloop<S, BK / 16, SPREAD ? BK / 16 : 0>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, KS, SPREAD ? KS : 0>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
@@ -578,10 +580,10 @@ static hipError_t launch_splitp(const GemmParams& p, hipStream_t st) {
 }
 
 template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false,
-          bool POISON = false>
+          bool POISON = false, int MI = 32>
 static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD, POISON>), dim3(grid), dim3(WM * WN * 64),
+    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD, POISON, MI>), dim3(grid), dim3(WM * WN * 64),
                        p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -1011,10 +1013,6 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             break;
         case 24:  // tile 23 with each slab's copies spread over the k-steps (S = 1: one slot,
                   // the slab's copies go out together, as in tile 23)
-            if constexpr (std::is_same<T, __bf16>::value) {   // the LDS-poisoning debug variant
-                if (p.poison && S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, true>(p, st);
-                if (p.poison && S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, true>(p, st);
-            }
             if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true>(p, st);
             if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true>(p, st);
             break;
@@ -1036,6 +1034,18 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             }
             if (S == 1) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
+            break;
+        case 31:  // tile 24 with 16x16x32 instructions (the default 256x256 tile)
+            if constexpr (std::is_same<T, __bf16>::value) {   // the LDS-poisoning debug variant
+                if (p.poison && S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, true, 16>(p, st);
+                if (p.poison && S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, true, 16>(p, st);
+            }
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, false, 16>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, false, 16>(p, st);
+            break;
+        case 32:  // tile 29 (192x256) with 16x16x32 instructions
+            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true, false, 16>(p, st);
+            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, true, false, 16>(p, st);
             break;
         case 29:  // tile 27 (192x256) with each slab's copies spread over the k-steps
             if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true>(p, st);
