@@ -98,9 +98,17 @@ struct MfmaCompute {
         const int lane = lane_id();
         const int r = lane % MI;
         const int g = lane / MI;
+        // k-chunk of lane group g within the k-step.  The instruction sums over all of its
+        // k, so any one-to-one assignment works as long as A and B use the same one (each
+        // accumulator still sees a fixed k order).  16x16x32: groups 0..3 take chunks
+        // 0, 2, 1, 3 -- with chunks 0..3 in lane order every 16-byte fragment read met a
+        // bank conflict on the 128-byte swizzled rows (lanes 0..31 then read two adjacent
+        // chunks of 16 rows; a probe of the patterns measured 100% conflicts for that and
+        // none for this order, as for the 32x32x16 reads).
+        const int kc = MI == 16 ? (g & 1) * 2 + (g >> 1) : g;
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            const int c = LG * ks + g;
+            const int c = LG * ks + kc;
             const int sw = c ^ swz<CPR>(r);  // wave-tile rows are multiples of 16: swz period 16
             a_off[ks] = (uint32_t)((wm * WTM + r) * ROWB + (sw << 4));
             b_off[ks] = (uint32_t)(A_BYTES + (wn * WTN + r) * ROWB + (sw << 4));
