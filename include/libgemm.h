@@ -19,7 +19,8 @@
  *
  * Arithmetic: products of the inputs are accumulated in fp32.  FP32 inputs use one
  *   fused multiply-add chain per output in ascending k (VALU path).  bf16 / f16 inputs
- *   use the matrix cores (v_mfma_f32_32x32x16_{bf16,f16}).  The epilogue computes, in
+ *   use the matrix cores (v_mfma_f32_16x16x32_{bf16,f16} in the default 256x256 and
+ *   192x256 tiles, v_mfma_f32_32x32x16_{bf16,f16} in the others).  The epilogue computes, in
  *   fp32, alpha*acc when beta == 0 (C is then never read, so NaN in C does not leak)
  *   and fmaf(alpha, acc, beta*C) otherwise, then rounds to the C type with
  *   round-to-nearest-even.  f16 subnormal inputs are not flushed.  The k order seen by
