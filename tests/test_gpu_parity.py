@@ -271,11 +271,28 @@ def test_bit_identical_across_stage_counts(case):
     assert err <= TOL[dtype]
 
 
-def test_xcd_order_does_not_change_results():
-    p = problem("bf16", "bf16", 2048, 2048, 512, ROW, COL, dist="normal", seed=12)
-    a = run(p)
-    b = run(p, flags=lg.GEMM_FLAG_NO_XCD_REMAP)
-    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+@pytest.mark.parametrize("M,N,K,la,lb,opts", [
+    (2048, 2048, 512, ROW, COL, {}),                                             # 64 tiles
+    (2000, 1504, 300, ROW, ROW, dict(kernel=K_MFMA_RING, tile=30, nstage=2)),    # row-major ring, 11 x 6 = 66 tiles
+    (1000, 1100, 256, ROW, COL, {}),                                             # 4 x 5 = 20 tiles
+    (2304, 2304, 256, ROW, COL, dict(kernel=K_MFMA_RING, tile=28, nstage=2)),    # persistent, 81 tiles
+    (4352, 4352, 128, ROW, COL, dict(kernel=K_MFMA_RING, tile=28, nstage=2)),    # persistent, 289 tiles > grid
+    (1100, 700, 96, ROW, ROW, dict(kernel=K_VALU_RING, tile=5, nstage=2)),       # fp32, 9 x 11 = 99 tiles
+])
+def test_xcd_order_does_not_change_results(M, N, K, la, lb, opts):
+    """The XCD remap (applied when the tile count is a multiple of 8) permutes the tiles:
+    every tile is written (C starts as NaN) and the bits equal those of plain order, for
+    plain, persistent (more tiles than workgroups) and fp32 grids, with tile counts that are
+    and are not multiples of 8."""
+    fp32 = opts.get("kernel") == K_VALU_RING
+    dt = "f32" if fp32 else "bf16"
+    p = problem(dt, dt, M, N, K, la, lb, dist="normal", seed=12)
+    say(f"[xcd] {M}x{N}x{K} {opts}")
+    a = run(p, **opts)
+    b = run(p, flags=lg.GEMM_FLAG_NO_XCD_REMAP, **opts)
+    view = torch.int32 if fp32 else torch.int16
+    assert not torch.isnan(a.float()).any()
+    assert torch.equal(a.view(view), b.view(view))
 
 
 # --------------------------------------------------------------- fp32 fma-chain model
