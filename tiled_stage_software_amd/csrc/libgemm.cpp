@@ -72,8 +72,8 @@ const Tile kMfmaRing[] = {
     {28, 256, 256, 64, 512, S2, 2, (256 + 256) * 64 * 2},         // tile 23, persistent
     {29, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 23's scheme, 2x4 waves of 96x64, copies spread
     {30, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 29 on row-major A (any pitch) and row-major B
-    {31, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 24 with 16x16x32 instructions (default)
-    {32, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 29 with 16x16x32 instructions
+    {31, 256, 256, 64, 512, S1 | S2, 2, (256 + 256) * 64 * 2},    // tile 23, 16x16x32, copies right after the barrier (default)
+    {32, 192, 256, 64, 512, S1 | S2, 2, (192 + 256) * 64 * 2},    // tile 31's scheme on 192x256
 #ifdef GEMM_ALL_TILES  // variants that lose on every workload measured (built on request)
     {4, 256, 256, 64, 256, S2, 2, (256 + 256) * 64 * 2},          // copies spread over the slab
     {5, 256, 256, 32, 256, S3 | S4, 3, (256 + 256) * 32 * 2},     // copies spread
@@ -97,10 +97,11 @@ const Tile kMfmaRing[] = {
 };
 // The MFMA ring tile used when none is named for a problem of >= 128 256x256 tiles (and
 // the cost model below keeps 256x256): 256x256x64, two slots, eight waves (2x4 of
-// 128x64, two per SIMD) of which one per SIMD issues the copies, each slab's copies
-// spread over its k-steps, 16x16x32 instructions (the fastest measured on 8192^3 bf16 and
-// on the f16 MLP shape: 2% and 4% ahead of the same tile with 32x32x16 instructions, tile
-// 24, which is itself 2% ahead of issuing each slab's copies together, tile 23).
+// 128x64, two per SIMD) of which one per SIMD issues the copies, 16x16x32 instructions,
+// and each slab's copies issued together in the k-step right after the barrier that frees
+// its slot (the fastest measured on 8192^3 bf16: 3% ahead of splitting them over the two
+// k-steps, 8% ahead of issuing them in the slab's first k-step; on the f16 MLP shape
+// within 1% of the split; the 32x32x16 form of the tile, 24, is 2-7% behind).
 constexpr int kMfmaRingDefault = 31;
 
 const Tile kMfmaStaged[] = {

@@ -450,7 +450,7 @@ struct SplitCopyOps : MfmaCompute<T, BM, BN, BK, WM, WN, MI> {
     __device__ __forceinline__ void math(int) { C::template math<BUF, (COPY && HAS) ? (L + PARTS - 1) / PARTS : 0>(); }
 };
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD, bool POISON,
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, int PARTS, bool POISON,
           int MI>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void mfma_split_kernel(const GemmParams p) {
@@ -478,7 +478,7 @@ void mfma_split_kernel(const GemmParams p) {
         ops.init((LDS_AS char*)(smem_raw));
         ops.la.init(p.A + (int64_t)m0 * p.lda * 2, p.lda * 2, BK * 2);
         ops.lb.init(p.B + (int64_t)n0 * p.ldb * 2, p.ldb * 2, BK * 2);
-        gemm_sched::ring_mainloop<S, KS, SPREAD ? KS : 0>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, KS, PARTS>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
@@ -486,7 +486,7 @@ void mfma_split_kernel(const GemmParams p) {
     } else {
         MaybePoison<POISON, SplitCopyOps<T, BM, BN, BK, WM, WN, S, NC, false, MI>> ops;
         ops.init((LDS_AS char*)(smem_raw));
-        gemm_sched::ring_mainloop<S, KS, SPREAD ? KS : 0>(ops, p.K / BK);
+        gemm_sched::ring_mainloop<S, KS, PARTS>(ops, p.K / BK);
         if constexpr (LDS_EPI) {
             if (lds_epi) { ops.template epilogue_lds<OUT, WM * WN * 64>(p, m0, n0); return; }
         }
@@ -587,11 +587,11 @@ static hipError_t launch_splitp(const GemmParams& p, hipStream_t st) {
     return hipGetLastError();
 }
 
-template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, bool SPREAD = false,
+template <typename T, int OUT, int BM, int BN, int BK, int WM, int WN, int S, int NC, int PARTS = 0,
           bool POISON = false, int MI = 32>
 static hipError_t launch_split(const GemmParams& p, hipStream_t st) {
     const int grid = p.tiles_m * p.tiles_n;
-    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, SPREAD, POISON, MI>), dim3(grid), dim3(WM * WN * 64),
+    hipLaunchKernelGGL((mfma_split_kernel<T, OUT, BM, BN, BK, WM, WN, S, NC, PARTS, POISON, MI>), dim3(grid), dim3(WM * WN * 64),
                        p.lds_pad, st, p);
     return hipGetLastError();
 }
@@ -1019,14 +1019,14 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4>(p, st);
             break;
-        case 24:  // tile 23 with each slab's copies spread over the k-steps (S = 1: one slot,
+        case 24:  // tile 23 with each slab's copies spread over its 4 k-steps (S = 1: one slot,
                   // the slab's copies go out together, as in tile 23)
-            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true>(p, st);
-            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true>(p, st);
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, 4>(p, st);
             break;
         case 25:  // 256x256x32, 2x4 waves, copies by waves 0-3 spread, deeper ring
-            if (S == 3) return launch_split<T, OUT, 256, 256, 32, 2, 4, 3, 4, true>(p, st);
-            if (S == 4) return launch_split<T, OUT, 256, 256, 32, 2, 4, 4, 4, true>(p, st);
+            if (S == 3) return launch_split<T, OUT, 256, 256, 32, 2, 4, 3, 4, 2>(p, st);
+            if (S == 4) return launch_split<T, OUT, 256, 256, 32, 2, 4, 4, 4, 2>(p, st);
             break;
         case 26:  // 256x192x64, 4x2 waves of 64x96, copies by waves 0-3 only
             if (S == 1) return launch_split<T, OUT, 256, 192, 64, 4, 2, 1, 4>(p, st);
@@ -1043,21 +1043,22 @@ hipError_t ring_dispatch(int tile, int S, const GemmParams& p, hipStream_t st) {
             if (S == 1) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 1, 4>(p, st);
             if (S == 2) return launch_kn<T, OUT, 192, 256, 64, 2, 4, 2, 4>(p, st);
             break;
-        case 31:  // tile 24 with 16x16x32 instructions (the default 256x256 tile)
+        case 31:  // tile 23 with 16x16x32 instructions, each slab's copies issued together right
+                  // after the barrier that frees its slot (the default 256x256 tile)
             if constexpr (std::is_same<T, __bf16>::value) {   // the LDS-poisoning debug variant
-                if (p.poison && S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, true, 16>(p, st);
-                if (p.poison && S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, true, 16>(p, st);
+                if (p.poison && S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, 1, true, 16>(p, st);
+                if (p.poison && S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, 1, true, 16>(p, st);
             }
-            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, true, false, 16>(p, st);
-            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, true, false, 16>(p, st);
+            if (S == 1) return launch_split<T, OUT, 256, 256, 64, 2, 4, 1, 4, 1, false, 16>(p, st);
+            if (S == 2) return launch_split<T, OUT, 256, 256, 64, 2, 4, 2, 4, 1, false, 16>(p, st);
             break;
-        case 32:  // tile 29 (192x256) with 16x16x32 instructions
-            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true, false, 16>(p, st);
-            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, true, false, 16>(p, st);
+        case 32:  // tile 31's scheme on 192x256
+            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, 1, false, 16>(p, st);
+            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, 1, false, 16>(p, st);
             break;
-        case 29:  // tile 27 (192x256) with each slab's copies spread over the k-steps
-            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, true>(p, st);
-            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, true>(p, st);
+        case 29:  // tile 27 (192x256) with each slab's copies spread over its 4 k-steps
+            if (S == 1) return launch_split<T, OUT, 192, 256, 64, 2, 4, 1, 4, 4>(p, st);
+            if (S == 2) return launch_split<T, OUT, 192, 256, 64, 2, 4, 2, 4, 4>(p, st);
             break;
 #ifdef GEMM_ALL_TILES
         case 4:  // 256x256x64, 2x2 waves, copies spread over the whole slab
