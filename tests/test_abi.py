@@ -119,9 +119,13 @@ def test_plans_for_the_workloads():
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (128, 64)
     assert p.grid == 32 * 64 and p.tile == 5 and p.threads == 256 and p.nstage == 4
-    # fp32 256^3 NN -> direct ring, small tile
+    # fp32 256^3 NN -> direct ring, 16x16 tiles (64 of 32x32 would leave most CUs idle)
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (32, 32)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (16, 16)
+    assert p.tile == 9 and p.threads == 64 and p.grid == 256 and p.nstage == 4
+    # fp32 1024^3 NN: 1024 tiles of 32x32, four per CU -> the 32x32 tile
+    s, p = plan(F32, F32, ROW, ROW, 1024, 1024, 1024)
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and p.tile == 7 and (p.bm, p.bn) == (32, 32)
     # bf16 8192^3 NT -> MFMA ring, 256x256 split-copy tile (8 waves), two slots
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_MFMA_RING and (p.bm, p.bn, p.bk) == (256, 256, 64)
@@ -467,5 +471,5 @@ def test_poison_flag_is_planned_only_where_its_variant_is_built():
     for S in (1, 2, 3, 4):
         assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, flags=P)[0] == 0
     assert plan(F16, F16, ROW, COL, 8192, 8192, 8192, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED   # not built for f16
-    assert plan(F32, F32, ROW, ROW, 256, 256, 256, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED      # small tile 7
+    assert plan(F32, F32, ROW, ROW, 256, 256, 256, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED      # small tile 9
     assert plan(BF16, BF16, COL, COL, 512, 512, 512, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # staged kernel

@@ -304,6 +304,8 @@ def test_xcd_order_does_not_change_results(M, N, K, la, lb, opts):
     (K_VALU_RING, 4, 2, 256, 192, 256, ROW, ROW),
     (K_VALU_RING, 6, 4, 384, 128, 320, ROW, ROW),
     (K_VALU_RING, 7, 2, 256, 256, 256, ROW, ROW),
+    (K_VALU_RING, 9, 4, 272, 208, 224, ROW, ROW),    # 16x16 tiles, 17 x 13 of them
+    (K_VALU_RING, 9, 1, 40, 56, 96, ROW, ROW),       # ragged: edge tiles shifted inward
     (K_VALU_RING, 2, 1, 192, 128, 64, ROW, ROW),
     (K_VALU_STAGED, 1, 2, 131, 77, 50, COL, COL),
     (K_VALU_STAGED, 3, 1, 45, 33, 19, ROW, COL),
@@ -510,7 +512,7 @@ def test_ring_tiles_on_ragged_edges(ts):
         assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
 
 
-@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2), (7, 2)])
+@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2), (7, 2), (9, 4), (9, 2)])
 def test_valu_ring_on_ragged_edges(tile, S):
     """fp32 direct ring with M and N not multiples of the tile (N a multiple of 4, so the
     shifted last column tile stays 16-byte aligned; row pitch padded): edge tiles shifted

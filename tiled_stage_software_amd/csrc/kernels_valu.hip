@@ -285,6 +285,7 @@ hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream
         case 6: return ring_stages<128, 64, 16, 4, 8>(nstage, p, st);  // 256 threads, 4x8 per thread
         case 7: return ring_stages<32, 32, 32, 4, 4>(nstage, p, st);   // tile 3 with 32-deep slabs
         case 8: return ring_stages<128, 64, 32, 8, 4>(nstage, p, st);  // tile 5 with 32-deep slabs
+        case 9: return ring_stages<16, 16, 32, 1, 4>(nstage, p, st);   // 64 threads of 1x4
     }
     return hipErrorInvalidValue;
 }

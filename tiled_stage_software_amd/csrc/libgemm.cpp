@@ -51,6 +51,7 @@ const Tile kValuRing[] = {
     {6, 128, 64, 16, 256, S1 | S2 | S3 | S4, 2, (128 * 16 + 16 * 64) * 4},  // 4x8 per thread
     {7, 32, 32, 32, 64, S1 | S2 | S3 | S4, 2, (32 * 32 + 32 * 32) * 4},     // tile 3, 32-deep slabs
     {8, 128, 64, 32, 256, S1 | S2 | S3 | S4, 2, (128 * 32 + 32 * 64) * 4},  // tile 5, 32-deep slabs
+    {9, 16, 16, 32, 64, S1 | S2 | S3 | S4, 4, (16 * 32 + 32 * 16) * 4},     // 1x4 per thread, for grids too small for tile 7
 };
 // The fp32 ring tile used for problems of >= 512 128x64 tiles: 256 threads of 8x4, 4-k
 // steps, four slots (the fastest measured on fp32 4096^3 NN, 1-2% ahead of three).
@@ -315,9 +316,14 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
         // Automatic: the direct ring when the operands allow it, else the staged loader.
         if (!mfma) {
             // small problems: 32x32 tiles with 32-deep slabs (half the barriers of the
-            // 16-deep tile 3; fp32 256^3 11.9 vs 12.3 us)
+            // 16-deep tile 3; fp32 256^3 11.9 vs 12.3 us); while those would be fewer than
+            // three per compute unit, 16x16 tiles, each thread one row of four columns, so
+            // that every compute unit holds work (one wave per workgroup; fp32 NN 256^3
+            // 5.5 vs 11.8 us, 512^3 9.9 vs 21.4, 768^3 23 vs 32; at 1024^3, four 32x32
+            // tiles per unit, 45 vs 41)
             const Tile* big = find_tile(kValuRing, kValuRingDefault);
-            const Tile* small = find_tile(kValuRing, 7);
+            const bool tiny = cdiv(q.M, 32) * cdiv(q.N, 32) < 3 * int64_t(gemm::num_compute_units());
+            const Tile* small = find_tile(kValuRing, tiny ? 9 : 7);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
             const Tile* pick = (opts.tile ? find_tile(kValuRing, opts.tile) : (many ? big : small));
             if (pick && ring_ok(q, *pick, false, &why)) { kernel = GEMM_KERNEL_VALU_RING; t = pick; }
