@@ -24,6 +24,7 @@ import hashlib
 import glob
 import json
 import os
+import re
 import sys
 import time
 from typing import Optional
@@ -49,14 +50,28 @@ WORKLOAD_NAME = {
 }
 
 
+def _code_only(text: str) -> str:
+    """Source text without its comments and blank lines: an edit of a comment leaves the
+    compiled kernels, and so the counters taken on them, as they were."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    out = []
+    for line in text.splitlines():
+        cut = line.find("//")
+        line = (line if cut < 0 else line[:cut]).rstrip()
+        if line.strip():
+            out.append(line)
+    return "\n".join(out)
+
+
 def kernel_source_hash() -> str:
-    """Hash of the device sources (the .hip kernels and the headers they include); host
-    code that only chooses among kernels is covered by the plan check in traffic_for."""
+    """Hash of the device sources (the .hip kernels and the headers they include, comments
+    left out); host code that only chooses among kernels is covered by the plan check in
+    traffic_for."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tiled_stage_software_amd", "csrc")
     for f in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.hpp"))):
-        with open(f, "rb") as fh:
-            h.update(os.path.basename(f).encode() + fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(os.path.basename(f).encode() + _code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -652,8 +652,8 @@ struct MfmaKnCompute : MfmaCompute<T, BM, BN, BK, WM, WN, 32> {
 
 // Split-copy ring over a row-major A of any alignment and a row-major B read in place.
 // The copying waves (one per SIMD) bring each K-slab in two ways: B's BK rows by direct
-// global->LDS copies (16-byte aligned rows, spread over the slab like the other split
-// tiles); A's BM rows through registers, with 16-byte loads of any alignment issued as
+// global->LDS copies (16-byte aligned rows, one part per k-step of the slab: the part
+// count moves this kernel by under half a percent); A's BM rows through registers, with 16-byte loads of any alignment issued as
 // soon as the slot is free and written into it just before the barrier that publishes the
 // slab (the staged half of the protocol).  A K tail needs no padding: A's columns beyond K
 // are cleared in registers, and in the last, partial slab the lanes of B's copies whose
