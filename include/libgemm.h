@@ -117,7 +117,7 @@ typedef struct gemm_opts {
  * overwrites the slot with all-ones bits (NaN in bf16, f16 and fp32) and meets at a second
  * barrier before the next copy into it is issued, so a pipeline that read a slot outside
  * its live range would produce NaN instead of a plausible stale value.  Built for the
- * default tiles only -- fp32 ring tile 5 (nstage 1-4), bf16 ring tiles 24 and 30 (nstage
+ * default tiles only -- fp32 ring tile 5 (nstage 1-4), bf16 ring tiles 31 and 30 (nstage
  * 1, 2) -- and not for the kernels that run on rewritten operands in the workspace path;
  * any other plan with this flag is GEMM_ERR_UNSUPPORTED.  Results are unchanged; the
  * extra stores and barrier per slab make it slower. */
