@@ -29,9 +29,11 @@
  *
  * Pointers: A, B and C are DEVICE pointers owned by the caller.  The library allocates
  *   nothing, keeps no pointer after returning and holds no mutable global state apart
- *   from a thread-local error string and a per-device cache of the compute-unit count
- *   (atomic: first calls from several threads at once are safe); calls are reentrant
- *   and may come from any number of host threads.  C must not overlap A or B
+ *   from a thread-local error string, a per-device cache of the compute-unit count and,
+ *   for gemm_ws_static only, that entry's static device workspace and a per-device cache
+ *   of its address (the caches are atomic: first calls from several threads at once are
+ *   safe); calls are reentrant and may come from any number of host threads (calls of
+ *   gemm_ws_static that may overlap on one GPU must be serialised, see there).  C must not overlap A or B
  *   (not checked).  Misaligned pointers or leading dimensions are never an error: they
  *   select a slower load path, or, given a caller-owned workspace (gemm_*_ws), a
  *   one-pass rewrite of the operands for the fast path.  (gemm_h2d_staged alone takes
