@@ -244,6 +244,44 @@ def pipe_copy_control(dev, mib: int = 1024, reps: int = 20):
             "nstage": out, "copy_exact": ok, "plain_device_copy": anchor, "hbm_peak_GB/s": 8000}
 
 
+def mfma_ceiling_control(dev, grid: int = 1024, iters: int = 4000, reps: int = 10, warmup: int = 5):
+    """The compute-bound control: TFLOP/s of matrix instructions on register operands (no
+    memory traffic in the loop) for the instruction shape and operand distribution of the
+    bf16 and f16 workloads, and on zeros.  What separates these figures is the clock the
+    card's power limit allows for that data, so a GEMM kernel's fraction of the figure for
+    its own shape and distribution is what its feed and overlap lose."""
+    st = torch.cuda.current_stream(dev)
+    n_frag = lg.GEMM_CEIL_FRAG_ELEMS
+    sums = torch.empty(grid * lg.GEMM_CEIL_THREADS, dtype=torch.float32, device=dev)
+    flops = grid * (lg.GEMM_CEIL_THREADS // 64) * iters * float(1 << 20)
+    g = torch.Generator().manual_seed(4242)
+    normal = torch.randn((n_frag,), generator=g)
+    cases = [("bf16 16x16x32, N(0,1) (the bf16 square workload's operands)", lg.GEMM_BF16, 16, normal),
+             ("bf16 16x16x32, zeros", lg.GEMM_BF16, 16, torch.zeros(n_frag)),
+             ("bf16 32x32x16, N(0,1)", lg.GEMM_BF16, 32, normal),
+             ("f16 16x16x32, N(0,1)/64 (the f16 MLP workload's operands)", lg.GEMM_F16, 16, normal / 64)]
+    out = {}
+    for what, t, shape, vals in cases:
+        dt = torch.bfloat16 if t == lg.GEMM_BF16 else torch.float16
+        frags = vals.to(dt).view(torch.int16).to(dev)
+        for _ in range(warmup):
+            lg.check(lg.gemm_mfma_ceiling(t, shape, frags.data_ptr(), sums.data_ptr(), grid, iters, st.cuda_stream))
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        for _ in range(reps):
+            lg.gemm_mfma_ceiling(t, shape, frags.data_ptr(), sums.data_ptr(), grid, iters, st.cuda_stream)
+        e1.record(st)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tf = flops / (ms * 1e-3) / 1e12
+        out[what] = {"ms": round(ms, 3), "tflops": round(tf, 1), "frac_of_peak": round(tf / PEAK["bf16"], 4),
+                     "finite": bool(torch.isfinite(sums).all())}
+    del sums
+    return {"what": f"matrix instructions on register operands, {grid} workgroups of 8 waves, {iters} rounds of "
+                    "2^20 FLOPs per wave", "cases": out}
+
+
 def h2d_staging_control(dev, mib: int = 256, chunk_mib: int = 4, reps: int = 3):
     """Host-to-device copy of `mib` MiB of ordinary (pageable) host memory through the
     page-locked staging ring of gemm_h2d_staged, per slot count (wall clock: the call
@@ -454,6 +492,9 @@ def main():
     ap.add_argument("--vendor", action="store_true",
                     help="with --only: time the vendor BLAS (torch.mm) on the workload instead of this "
                          "library (for profiling the vendor kernel beside ours)")
+    ap.add_argument("--mfma-control", action="store_true",
+                    help="run only the compute-bound control (matrix instructions on register operands) "
+                         "and print its figures (for a counter pass of the control alone)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy kernel of this many MiB "
                          "(read + write) a few times: the reference for scaling HBM counters")
@@ -481,6 +522,9 @@ def main():
         return
     lg.load()
     src_hash = kernel_source_hash()
+    if args.mfma_control:
+        print(json.dumps({"mfma_control": mfma_ceiling_control(dev), "kernel_source_hash": src_hash}), flush=True)
+        return
 
     w = Workload(args.config, dev)
     opts = dict(nstage=args.nstage, kernel=args.kernel, tile=args.tile)
@@ -533,6 +577,7 @@ def main():
         # clock); the headline workload's own sweep comes last, so that its timed launches
         # follow GPU work without a pause
         rec["negative_control"] = pipe_copy_control(dev)
+        rec["mfma_control"] = mfma_ceiling_control(dev)
         rec["h2d_staging"] = h2d_staging_control(dev)
         sweep = {}
         parity = {}
@@ -604,6 +649,10 @@ def main():
     # the headline's timed launches, right after the sweep has brought the card to its
     # steady clock (no host-side work in between)
     headline()
+    if "mfma_control" in rec and rec["dtype"] in ("bf16", "f16"):
+        key = [k for k in rec["mfma_control"]["cases"] if k.startswith(rec["dtype"] + " 16x16x32, N(0,1)")][0]
+        ctl = rec["mfma_control"]["cases"][key]["tflops"]
+        rec["frac_of_mfma_control"] = {"control": key, "control_tflops": ctl, "frac": round(rec["value"] / ctl, 4)}
 
     if not args.no_sweep and args.config in ("c3", "c4") and not args.no_cpu_baseline:
         parity[args.config] = oracle_parity(w, args.full_oracle)

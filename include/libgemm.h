@@ -119,7 +119,7 @@ typedef struct gemm_opts {
  * overwrites the slot with all-ones bits (NaN in bf16, f16 and fp32) and meets at a second
  * barrier before the next copy into it is issued, so a pipeline that read a slot outside
  * its live range would produce NaN instead of a plausible stale value.  Built for the
- * default tiles only -- fp32 ring tile 5 (nstage 1-4), bf16 ring tiles 31 and 30 (nstage
+ * default tiles only -- fp32 ring tiles 5 and 10 (nstage 1-4), bf16 ring tiles 31 and 30 (nstage
  * 1, 2) -- and not for the kernels that run on rewritten operands in the workspace path;
  * any other plan with this flag is GEMM_ERR_UNSUPPORTED.  Results are unchanged; the
  * extra stores and barrier per slab make it slower. */
@@ -308,6 +308,36 @@ int gemm_schedule(int kernel, int nstage, int num_k, int ksteps, int* events, in
  * Errors: GEMM_ERR_INVALID_ARG (size, alignment, NULL, overlap), GEMM_ERR_UNSUPPORTED
  * (nstage), GEMM_ERR_HIP (launch). */
 gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nstage, hipStream_t stream);
+
+/* The compute-bound control, the counterpart of gemm_pipe_copy: matrix instructions on
+ * operands held in registers, with no memory access inside the loop, so that its rate is
+ * what the matrix cores sustain at the clock the card settles at for that operand data.
+ * Set beside a GEMM kernel on operands of the same distribution, it separates what the
+ * kernel's feed and overlap lose from what the card cannot give (the page "CUTLASS-Cute
+ * 初步(6)", sections 7 and 7.1: more stages fill the gaps between math phases, up to the
+ * math rate and never past it).
+ * Each of `grid` workgroups runs GEMM_CEIL_THREADS threads (8 waves, two per SIMD).  Every
+ * wave reads the whole fragment set once: fragment f, lane l, element e at
+ * frags[(f*64 + l)*8 + e] (GEMM_CEIL_FRAG_ELEMS 16-bit values of type in_type).  Fragment
+ * f = r*(WA + WB) + i is the first operand of instruction row i of k-step r (i < WA), and
+ * f = r*(WA + WB) + WA + j the second operand of column j; lane l of a fragment holds row
+ * l mod MI, k = 8*(l / MI) .. +7, of its MI-row block.  shape 16: v_mfma_f32_16x16x32,
+ * R = 4, WA = WB = 4; shape 32: v_mfma_f32_32x32x16, R = 8, WA = WB = 2.  The wave then
+ * runs `iters` rounds of: for each k-step r, acc[i][j] += X(r,i) * Y(r,j)^T for all i, j
+ * (X, Y the MI x KI blocks of fragments (r,i) and (r,j)) -- 2^20 FLOPs per wave and round,
+ * so the call does grid * 8 * iters * 2^20 FLOPs.  Finally lane l of wave w of workgroup g
+ * writes sums[(g*8 + w)*64 + l] = the sum, in a fixed order, of the accumulator values it
+ * holds (for shape 32, registers 4q+t hold rows 8q + 4*(l/32) + t of column l mod 32 of
+ * each accumulator; for shape 16, register t holds row 4*(l/16) + t of column l mod 16).
+ * frags: device, 16-byte aligned, read-only; sums: device, grid * 512 floats, 4-byte
+ * aligned; grid 1..GEMM_CEIL_MAX_GRID; iters >= 0 (0 writes zeros).  Enqueued on `stream`.
+ * Errors: GEMM_ERR_UNSUPPORTED (in_type, shape), GEMM_ERR_INVALID_ARG (grid, iters, NULL,
+ * alignment), GEMM_ERR_HIP (launch). */
+#define GEMM_CEIL_THREADS 512
+#define GEMM_CEIL_FRAG_ELEMS 16384
+#define GEMM_CEIL_MAX_GRID 65536
+gemm_status_t gemm_mfma_ceiling(int in_type, int shape, const void* frags, float* sums, int64_t grid, int64_t iters,
+                                hipStream_t stream);
 
 /* dst[0, bytes) = src[0, bytes) from ordinary (pageable) host memory to the device,
  * staged through a ring of `nstage` page-locked slots of `chunk_bytes` each: the CPU

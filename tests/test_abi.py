@@ -115,10 +115,19 @@ def test_quick_returns():
 
 
 def test_plans_for_the_workloads():
-    # fp32 4096^3 NN -> direct ring, 128x64 tile
+    # fp32 4096^3 NN -> direct ring, 128x128 tile of 8x8 per thread: 1024 tiles, two full
+    # rounds of two workgroups per CU
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (128, 64)
-    assert p.grid == 32 * 64 and p.tile == 5 and p.threads == 256 and p.nstage == 4
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn, p.bk) == (128, 128, 32)
+    assert p.grid == 32 * 32 and p.tile == 10 and p.threads == 256 and p.nstage == 2
+    # the round model's other picks: 3072^3 -> 128x64 (576 tiles of 128x128 would leave a
+    # second round an eighth full), 2048^3 -> one 512-thread 128x128 tile per CU, and K not a
+    # multiple of 32 -> no tile 10
+    assert plan(F32, F32, ROW, ROW, 3072, 3072, 3072)[1].tile == 5
+    s, p = plan(F32, F32, ROW, ROW, 2048, 2048, 2048)
+    assert s == 0 and p.tile == 11 and p.threads == 512 and p.grid == 256 and p.nstage == 4
+    assert plan(F32, F32, ROW, ROW, 4096, 4096, 4080)[1].tile == 11
+    assert plan(F32, F32, ROW, ROW, 4096, 4096, 4112)[1].tile in (5, 11)
     # fp32 256^3 NN -> direct ring, 16x16 tiles (64 of 32x32 would leave most CUs idle)
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (16, 16)
@@ -212,6 +221,26 @@ def test_pipe_copy_rejects_bad_arguments_before_launching():
         assert lg.gemm_pipe_copy(dst, src, n, st) == want, (dst, src, n, st)
         assert lg.gemm_last_error()
     assert lg.gemm_pipe_copy(0, 0, 0, 2) == lg.GEMM_OK       # empty copy: nothing launched
+
+
+def test_mfma_ceiling_rejects_bad_arguments_before_launching():
+    """Every error path of gemm_mfma_ceiling returns before any HIP call (runs without a GPU)."""
+    cases = [
+        (lg.GEMM_F32, 16, A16, C16, 1, 1, lg.GEMM_ERR_UNSUPPORTED),     # fp32 has no matrix instruction here
+        (7, 16, A16, C16, 1, 1, lg.GEMM_ERR_UNSUPPORTED),
+        (BF16, 8, A16, C16, 1, 1, lg.GEMM_ERR_UNSUPPORTED),             # shape
+        (BF16, 64, A16, C16, 1, 1, lg.GEMM_ERR_UNSUPPORTED),
+        (BF16, 16, A16, C16, 0, 1, lg.GEMM_ERR_INVALID_ARG),            # grid
+        (BF16, 16, A16, C16, lg.GEMM_CEIL_MAX_GRID + 1, 1, lg.GEMM_ERR_INVALID_ARG),
+        (BF16, 16, A16, C16, 1, -1, lg.GEMM_ERR_INVALID_ARG),           # iters
+        (BF16, 16, 0, C16, 1, 1, lg.GEMM_ERR_INVALID_ARG),              # NULL
+        (BF16, 32, A16, 0, 1, 1, lg.GEMM_ERR_INVALID_ARG),
+        (lg.GEMM_F16, 16, A16 + 8, C16, 1, 1, lg.GEMM_ERR_INVALID_ARG),  # alignment
+        (lg.GEMM_F16, 32, A16, C16 + 2, 1, 1, lg.GEMM_ERR_INVALID_ARG),
+    ]
+    for t, shape, fr, sums, grid, iters, want in cases:
+        assert lg.gemm_mfma_ceiling(t, shape, fr, sums, grid, iters) == want, (t, shape, fr, sums, grid, iters)
+        assert lg.gemm_last_error()
 
 
 def test_tune_rejects_bad_arguments_before_launching():
@@ -383,6 +412,7 @@ def test_launch_without_a_device_reports_hip_error():
         ("gemm_bf16_ws pack", lambda: lg.gemm_bf16_ws(ROW, ROW, 4000, 3000, 2049, 0.5, A16, 2049, B16, 3000, 1.0,
                                                      C16, lg.GEMM_F32, 3000, 0, None, 0x40000000, 1 << 26)),
         ("gemm_pipe_copy", lambda: lg.gemm_pipe_copy(A16, 0x800000, 1 << 16, 2)),
+        ("gemm_mfma_ceiling", lambda: lg.gemm_mfma_ceiling(BF16, 16, A16, C16, 4, 1)),
     ]
     for name, call in cases:
         s = call()
@@ -457,7 +487,7 @@ def test_debug_env_prints_every_choice_and_error():
 
 
 def test_poison_flag_is_planned_only_where_its_variant_is_built():
-    """GEMM_FLAG_POISON_LDS: the default fp32 ring tile and the bf16 tiles 31 / 30 plan with
+    """GEMM_FLAG_POISON_LDS: the fp32 ring tiles 5 and 10 and the bf16 tiles 31 / 30 plan with
     it; anything else is refused before a launch."""
     P = lg.GEMM_FLAG_POISON_LDS
     s, p = plan(BF16, BF16, ROW, COL, 8192, 8192, 8192, flags=P)
@@ -467,9 +497,12 @@ def test_poison_flag_is_planned_only_where_its_variant_is_built():
     s, p = plan(BF16, F32, ROW, ROW, 4000, 3000, 2049, alpha=0.5, beta=1.0, lda=2049, flags=P)
     assert s == 0 and p.tile == 30
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096, flags=P)
-    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and p.tile == 5
+    assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and p.tile == 10
     for S in (1, 2, 3, 4):
         assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, flags=P)[0] == 0
+        assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, kernel=lg.GEMM_KERNEL_VALU_RING, tile=5, nstage=S,
+                    flags=P)[0] == 0
+    assert plan(F32, F32, ROW, ROW, 2048, 2048, 2048, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # tile 11
     assert plan(F16, F16, ROW, COL, 8192, 8192, 8192, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED   # not built for f16
     assert plan(F32, F32, ROW, ROW, 256, 256, 256, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED      # small tile 9
     assert plan(BF16, BF16, COL, COL, 512, 512, 512, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # staged kernel

@@ -58,6 +58,8 @@ FAMILIES = [  # (dtype, out, la, lb, kernel, tile, nstage, M, N, K): M, N, K >= 
     ("f32", "f32", ROW, ROW, K_VALU_RING, 1, 2, 256, 192, 128),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 5, 3, 256, 192, 128),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 6, 2, 256, 192, 128),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 10, 2, 256, 256, 128),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 11, 4, 256, 384, 128),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 3, 4, 96, 64, 48),
     ("f32", "f32", COL, COL, K_VALU_STAGED, 1, 2, 130, 70, 45),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 1, 2, 512, 512, 256),
@@ -200,6 +202,7 @@ def test_full_size_small_integers_bit_exact(name):
 
 
 FULL_STAGES = [  # (workload, kernel family, tile, stage counts): the default tiles at full size
+    ("c2", K_VALU_RING, 10, [1, 2, 3, 4]),
     ("c2", K_VALU_RING, 5, [1, 2, 3, 4]),
     ("c3", K_MFMA_RING, 31, [1, 2]),
     ("c4", K_MFMA_RING, 31, [1, 2]),
@@ -207,7 +210,7 @@ FULL_STAGES = [  # (workload, kernel family, tile, stage counts): the default ti
 ]
 
 
-@pytest.mark.parametrize("case", FULL_STAGES, ids=lambda c: c[0])
+@pytest.mark.parametrize("case", FULL_STAGES, ids=lambda c: f"{c[0]}-t{c[2]}")
 def test_full_shape_bit_identical_across_stage_counts(case):
     """At the full configuration shapes: the ring depth changes no bit of the output (every
     accumulator sees the same k order), and a repeated run changes none either."""
@@ -228,6 +231,8 @@ def test_full_shape_bit_identical_across_stage_counts(case):
 RING_STAGES = [
     ("f32", "f32", ROW, ROW, K_VALU_RING, 1, [1, 2, 3, 4], 512, 384, 1024),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 5, [1, 2, 3, 4], 512, 384, 1024),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 10, [1, 2, 3, 4], 520, 392, 1024),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 11, [1, 2, 3, 4], 384, 520, 512),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 4, [1, 2, 3, 4], 256, 320, 512),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 7, [1, 2, 3, 4], 96, 64, 320),
     ("f32", "f32", ROW, ROW, K_VALU_RING, 3, [1, 2, 3, 4], 96, 64, 160),
@@ -306,6 +311,10 @@ def test_xcd_order_does_not_change_results(M, N, K, la, lb, opts):
     (K_VALU_RING, 7, 2, 256, 256, 256, ROW, ROW),
     (K_VALU_RING, 9, 4, 272, 208, 224, ROW, ROW),    # 16x16 tiles, 17 x 13 of them
     (K_VALU_RING, 9, 1, 40, 56, 96, ROW, ROW),       # ragged: edge tiles shifted inward
+    (K_VALU_RING, 10, 2, 384, 256, 320, ROW, ROW),   # 128x128 tiles of 8x8 per thread
+    (K_VALU_RING, 10, 4, 300, 260, 96, ROW, ROW),    # ragged
+    (K_VALU_RING, 11, 4, 256, 384, 336, ROW, ROW),   # 128x128 tiles, 512 threads of 8x4
+    (K_VALU_RING, 11, 1, 260, 132, 48, ROW, ROW),    # ragged
     (K_VALU_RING, 2, 1, 192, 128, 64, ROW, ROW),
     (K_VALU_STAGED, 1, 2, 131, 77, 50, COL, COL),
     (K_VALU_STAGED, 3, 1, 45, 33, 19, ROW, COL),
@@ -512,12 +521,14 @@ def test_ring_tiles_on_ragged_edges(ts):
         assert np.array_equal(got.double().numpy(), expected_rounded(oracle_ref(p), p.out))
 
 
-@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2), (7, 2), (9, 4), (9, 2)])
+@pytest.mark.parametrize("tile,S", [(1, 2), (2, 3), (3, 1), (5, 3), (6, 2), (7, 2), (9, 4), (9, 2), (10, 2), (10, 3),
+                                    (11, 4), (11, 2)])
 def test_valu_ring_on_ragged_edges(tile, S):
     """fp32 direct ring with M and N not multiples of the tile (N a multiple of 4, so the
     shifted last column tile stays 16-byte aligned; row pitch padded): edge tiles shifted
     inward, every element stored once, exact."""
-    for (M, N, K, ldb) in ((300, 260, 64, 264), (130, 100, 32, 104)):
+    second = (130, 100, 32, 104) if tile not in (10, 11) else (260, 132, 96, 136)   # >= the 128x128 tiles
+    for (M, N, K, ldb) in ((300, 260, 64, 264), second):
         say(f"[ragged valu] tile={tile} S={S} {M}x{N}x{K} ldb={ldb}")
         p = problem("f32", "f32", M, N, K, ROW, ROW, dist="int2", seed=101, ldb=ldb)
         got = run(p, kernel=K_VALU_RING, tile=tile, nstage=S)
@@ -562,6 +573,7 @@ def test_row_major_ring_exact_on_tails_and_pitches(case):
 
 POISON_CASES = [  # (dtype, out, la, lb, kernel, tile, stages, M, N, K, alpha, beta): several slabs, ragged M / N
     ("f32", "f32", ROW, ROW, K_VALU_RING, 5, (1, 2, 3, 4), 300, 200, 160, 1.0, 0.0),
+    ("f32", "f32", ROW, ROW, K_VALU_RING, 10, (1, 2, 3, 4), 300, 200, 160, 1.0, 0.0),
     ("bf16", "bf16", ROW, COL, K_MFMA_RING, 31, (1, 2), 520, 600, 448, 1.0, 0.0),
     ("bf16", "f32", ROW, COL, K_MFMA_RING, 31, (1, 2), 300, 264, 320, 0.5, 1.0),
     ("bf16", "f32", ROW, ROW, K_MFMA_RING, 30, (1, 2), 400, 520, 449, 0.5, 1.0),

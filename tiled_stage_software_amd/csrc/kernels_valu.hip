@@ -276,6 +276,15 @@ hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream
         }
         return hipErrorInvalidValue;
     }
+    if (p.poison && tile == 10) {
+        switch (nstage) {
+            case 1: return launch_ring_poison<128, 128, 32, 8, 8, 1, 4>(p, st);
+            case 2: return launch_ring_poison<128, 128, 32, 8, 8, 2, 4>(p, st);
+            case 3: return launch_ring_poison<128, 128, 32, 8, 8, 3, 4>(p, st);
+            case 4: return launch_ring_poison<128, 128, 32, 8, 8, 4, 4>(p, st);
+        }
+        return hipErrorInvalidValue;
+    }
     switch (tile) {
         case 1: return ring_stages<128, 64, 16, 8, 8, 2>(nstage, p, st);  // 128 threads, 2-k steps (8-byte A reads)
         case 2: return ring_stages<64, 64, 16, 4, 4>(nstage, p, st);   // 256 threads
@@ -286,6 +295,8 @@ hipError_t launch_valu_ring(int tile, int nstage, const GemmParams& p, hipStream
         case 7: return ring_stages<32, 32, 32, 4, 4>(nstage, p, st);   // tile 3 with 32-deep slabs
         case 8: return ring_stages<128, 64, 32, 8, 4>(nstage, p, st);  // tile 5 with 32-deep slabs
         case 9: return ring_stages<16, 16, 32, 1, 4>(nstage, p, st);   // 64 threads of 1x4
+        case 10: return ring_stages<128, 128, 32, 8, 8>(nstage, p, st); // 256 threads, 8x8 per thread
+        case 11: return ring_stages<128, 128, 16, 8, 4>(nstage, p, st); // 512 threads, 8x4 per thread
     }
     return hipErrorInvalidValue;
 }

@@ -30,6 +30,14 @@ struct CopyParams {
 };
 hipError_t launch_pipe_copy(int nstage, const CopyParams& p, int64_t grid, hipStream_t st);
 
+// Matrix instructions on register operands (the compute-bound control): `grid` workgroups
+// of kCeilThreads; frags holds kCeilFrags fragments of 64 lanes x 8 16-bit values; sums one
+// float per thread.  mi = 16 or 32, in_type DT_BF16 or DT_F16.
+constexpr int kCeilThreads = 512;
+constexpr int kCeilFrags = 32;
+hipError_t launch_mfma_ceiling(int in_type, int mi, const uint16_t* frags, float* sums, int64_t grid, int64_t iters,
+                               hipStream_t st);
+
 // Operand repacking for the direct ring: dst is rows x len_pad 16-bit elements,
 // row-major, 16-byte aligned (len_pad a multiple of 64); dst[r][c] = src(r, c) for
 // c < len, +0 beyond, with src(r, c) = src[r*ld + c] (trans = 0) or src[c*ld + r]

@@ -52,9 +52,11 @@ const Tile kValuRing[] = {
     {7, 32, 32, 32, 64, S1 | S2 | S3 | S4, 2, (32 * 32 + 32 * 32) * 4},     // tile 3, 32-deep slabs
     {8, 128, 64, 32, 256, S1 | S2 | S3 | S4, 2, (128 * 32 + 32 * 64) * 4},  // tile 5, 32-deep slabs
     {9, 16, 16, 32, 64, S1 | S2 | S3 | S4, 4, (16 * 32 + 32 * 16) * 4},     // 1x4 per thread, for grids too small for tile 7
+    {10, 128, 128, 32, 256, S1 | S2 | S3 | S4, 2, (128 * 32 + 32 * 128) * 4},  // 8x8 per thread
+    {11, 128, 128, 16, 512, S1 | S2 | S3 | S4, 4, (128 * 16 + 16 * 128) * 4},  // 512 threads of 8x4
 };
-// The fp32 ring tile used for problems of >= 512 128x64 tiles: 256 threads of 8x4, 4-k
-// steps, four slots (the fastest measured on fp32 4096^3 NN, 1-2% ahead of three).
+// The fp32 ring tile forced kernels default to, and the reference size for the choice of
+// the large tile (valu_large_tile): 256 threads of 8x4, 4-k steps, four slots.
 constexpr int kValuRingDefault = 5;
 const Tile kValuStaged[] = {
     {1, 128, 64, 16, 128, S1 | S2, 2, (128 * 16 + 16 * 64) * 4},
@@ -258,6 +260,34 @@ bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
     return true;
 }
 
+// The fp32 ring tile for problems of at least 512 128x64 tiles.  A grid runs in rounds of
+// as many workgroups as are resident at once, so each candidate costs
+//   ceil(tiles / resident) rounds x resident x tile area / its full-occupancy rate,
+// with the residency and rate measured on fp32 squares of 4096-8192 (NN, S at the tile's
+// default): tile 5 (128x64, 256 threads of 8x4, 3 per CU) 97.5 TFLOP/s, tile 10 (128x128,
+// 256 threads of 8x8, 2 per CU) 100.8, tile 11 (128x128, 512 threads of 8x4, 1 per CU) 88.
+// The model picks the measured best on 2048^2x2048 (11: 85 against 73 for tile 5),
+// 3072^3 (5: 86 against 69 and 65), 4096^3 (10: 102 against 92), 8192^2x4096 (10),
+// 4000x3000x2048 and 6144x2048x4096 (5, by 2-8%).  Only tiles the direct ring accepts for
+// this problem compete (tile 10's 32-deep slabs need K % 32 == 0); tile 5 when none does.
+const Tile* valu_large_tile(const Problem& q) {
+    const int64_t cus = gemm::num_compute_units();
+    struct Cand { int id, per_cu; double rate; };
+    const Cand cand[] = {{5, 3, 97.5}, {10, 2, 100.8}, {11, 1, 88.0}};
+    const Tile* best = nullptr;
+    double best_cost = 0.0;
+    for (const Cand& c : cand) {
+        const Tile* t = find_tile(kValuRing, c.id);
+        const char* why = "";
+        if (!ring_ok(q, *t, false, &why)) continue;
+        const int64_t tiles = cdiv(q.M, t->bm) * cdiv(q.N, t->bn);
+        const int64_t resident = c.per_cu * cus;
+        const double cost = double(cdiv(tiles, resident)) * double(resident) * double(t->bm * t->bn) / c.rate;
+        if (!best || cost < best_cost) { best = t; best_cost = cost; }
+    }
+    return best ? best : find_tile(kValuRing, kValuRingDefault);
+}
+
 gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, GemmParams* gp) {
     gemm_opts_t opts = {0, 0, 0, 0};
     if (o) opts = *o;
@@ -325,6 +355,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
             const bool tiny = cdiv(q.M, 32) * cdiv(q.N, 32) < 3 * int64_t(gemm::num_compute_units());
             const Tile* small = find_tile(kValuRing, tiny ? 9 : 7);
             const bool many = cdiv(q.M, big->bm) * cdiv(q.N, big->bn) >= 512;
+            if (many) big = valu_large_tile(q);
             const Tile* pick = (opts.tile ? find_tile(kValuRing, opts.tile) : (many ? big : small));
             if (pick && ring_ok(q, *pick, false, &why)) { kernel = GEMM_KERNEL_VALU_RING; t = pick; }
             else {
@@ -403,7 +434,7 @@ gemm_status_t choose(const Problem& q, const gemm_opts_t* o, gemm_plan_t* plan, 
     }
     if (opts.flags & GEMM_FLAG_POISON_LDS) {
         // the debugging variant exists for the default tiles only (the launch tables)
-        const bool built = (kernel == GEMM_KERNEL_VALU_RING && t->id == 5) ||
+        const bool built = (kernel == GEMM_KERNEL_VALU_RING && (t->id == 5 || t->id == 10)) ||
                            (kernel == GEMM_KERNEL_MFMA_RING && q.in_type == gemm::DT_BF16 && (t->id == 31 || t->id == 30));
         if (!built)
             return fail(GEMM_ERR_UNSUPPORTED, "no LDS-poisoning build of kernel %d tile %d for this input type", kernel,
@@ -909,6 +940,26 @@ gemm_status_t gemm_pipe_copy(void* dst, const void* src, int64_t bytes, int nsta
     p.per_wg = (p.slabs + max_wg - 1) / max_wg;
     const int64_t grid = (p.slabs + p.per_wg - 1) / p.per_wg;
     const hipError_t e = gemm::launch_pipe_copy(nstage ? nstage : 2, p, grid, stream);
+    if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
+    return GEMM_OK;
+}
+
+gemm_status_t gemm_mfma_ceiling(int in_type, int shape, const void* frags, float* sums, int64_t grid, int64_t iters,
+                                hipStream_t stream) {
+    g_err[0] = 0;
+    if (in_type != GEMM_BF16 && in_type != GEMM_F16)
+        return fail(GEMM_ERR_UNSUPPORTED, "in_type %d: the matrix instructions take bf16 or f16", in_type);
+    if (shape != 16 && shape != 32) return fail(GEMM_ERR_UNSUPPORTED, "shape %d: 16 (16x16x32) or 32 (32x32x16)", shape);
+    if (grid < 1 || grid > GEMM_CEIL_MAX_GRID)
+        return fail(GEMM_ERR_INVALID_ARG, "grid %lld outside 1..%d", (long long)grid, GEMM_CEIL_MAX_GRID);
+    if (iters < 0) return fail(GEMM_ERR_INVALID_ARG, "iters %lld < 0", (long long)iters);
+    if (!frags || !sums) return fail(GEMM_ERR_INVALID_ARG, "null pointer");
+    if (!aligned16(frags)) return fail(GEMM_ERR_INVALID_ARG, "frags must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(sums) & 3) return fail(GEMM_ERR_INVALID_ARG, "sums must be 4-byte aligned");
+    static_assert(gemm::kCeilFrags * 64 * 8 == GEMM_CEIL_FRAG_ELEMS, "fragment set size");
+    static_assert(gemm::kCeilThreads == GEMM_CEIL_THREADS, "threads per workgroup");
+    const hipError_t e = gemm::launch_mfma_ceiling(in_type == GEMM_BF16 ? gemm::DT_BF16 : gemm::DT_F16, shape,
+                                                   static_cast<const uint16_t*>(frags), sums, grid, iters, stream);
     if (e != hipSuccess) return fail(GEMM_ERR_HIP, "launch failed: %s", hipGetErrorString(e));
     return GEMM_OK;
 }

@@ -29,13 +29,16 @@ GEMM_FLAG_EQUAL_LDS = 2
 GEMM_FLAG_POISON_LDS = 4
 GEMM_MAX_NSTAGE = 4
 GEMM_STATIC_WS_BYTES = 33554432
+GEMM_CEIL_THREADS = 512
+GEMM_CEIL_FRAG_ELEMS = 16384
+GEMM_CEIL_MAX_GRID = 65536
 
 KERNEL_NAMES = {0: "none", 1: "valu_ring", 2: "valu_staged", 3: "mfma_ring", 4: "mfma_staged", 5: "scale"}
 
 # Symbols declared in include/libgemm.h.
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_ex", "gemm_bf16_ex", "gemm_f16_ex",
            "gemm_bf16_ws", "gemm_f16_ws", "gemm_ws_static", "gemm_workspace_size", "gemm_plan", "gemm_tune", "gemm_tune_ws",
-           "gemm_schedule", "gemm_pipe_copy", "gemm_h2d_staged", "gemm_h2d_staged_async", "gemm_status_string",
+           "gemm_schedule", "gemm_pipe_copy", "gemm_mfma_ceiling", "gemm_h2d_staged", "gemm_h2d_staged_async", "gemm_status_string",
            "gemm_last_error")
 
 
@@ -108,6 +111,8 @@ def load():
         lib.gemm_tune_ws.restype = i32
         lib.gemm_pipe_copy.argtypes = [vp, vp, i64, i32, vp]
         lib.gemm_pipe_copy.restype = i32
+        lib.gemm_mfma_ceiling.argtypes = [i32, i32, vp, vp, i64, i64, vp]
+        lib.gemm_mfma_ceiling.restype = i32
         for name in ("gemm_h2d_staged", "gemm_h2d_staged_async"):
             getattr(lib, name).argtypes = [vp, vp, i64, vp, i64, i32, vp]
             getattr(lib, name).restype = i32
@@ -223,6 +228,13 @@ def gemm_tune_ws(in_type, c_type, la, lb, M, N, K, alpha, A, lda, B, ldb, beta, 
 def gemm_pipe_copy(dst: int, src: int, nbytes: int, nstage: int = 0, stream: int = 0) -> int:
     """dst[0, nbytes) = src[0, nbytes) through the nStage LDS ring (device pointers)."""
     return load().gemm_pipe_copy(dst, src, nbytes, nstage, stream)
+
+
+def gemm_mfma_ceiling(in_type: int, shape: int, frags: int, sums: int, grid: int, iters: int,
+                      stream: int = 0) -> int:
+    """Matrix instructions on register operands (device pointers): grid * 8 * iters * 2^20
+    FLOPs; one fp32 accumulator sum per thread into sums."""
+    return load().gemm_mfma_ceiling(in_type, shape, frags, sums, grid, iters, stream)
 
 
 def gemm_h2d_staged(dst: int, src: int, nbytes: int, staging: int, chunk_bytes: int, nstage: int = 2,
