@@ -282,6 +282,60 @@ def mfma_ceiling_control(dev, grid: int = 1024, iters: int = 4000, reps: int = 1
                     "2^20 FLOPs per wave", "cases": out}
 
 
+FP32_TILE_SHAPES = [(2048, 2048, 2048), (2560, 2560, 2560), (3072, 3072, 3072), (3584, 3584, 2048),
+                    (4096, 4096, 4096), (4096, 2048, 4096), (4096, 4096, 1024), (1536, 4096, 4096),
+                    (2048, 8192, 2048), (5120, 5120, 1024), (6144, 6144, 2048), (6144, 2048, 4096),
+                    (7168, 3072, 2048), (4000, 3000, 2048), (3000, 3000, 3008), (8192, 8192, 4096)]
+
+
+def fp32_tile_choice(dev, ms_target: float = 60.0):
+    """For fp32 NN problems of many shapes: TFLOP/s of each large fp32 ring tile forced (5:
+    128x64, 10: 128x128 of 8x8 per thread, 11: 128x128 of 512 threads), each at its default
+    stage count, then of the planner's own choice, in one run (each timed over about
+    `ms_target` ms after about half that of warm-up launches)."""
+    st = torch.cuda.current_stream(dev).cuda_stream
+    out = []
+    for (M, N, K) in FP32_TILE_SHAPES:
+        g = torch.Generator(device="cpu").manual_seed(M * 7 + N * 3 + K)
+        A = (torch.rand(M * K, generator=g) * 2 - 1).to(dev)
+        B = (torch.rand(K * N, generator=g) * 2 - 1).to(dev)
+        C = torch.empty(M * N, device=dev)
+
+        def tflops(opts):
+            def call():
+                return lg.gemm_f32_ex(0, 0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0.0, C.data_ptr(), N,
+                                      st, opts)
+            if call() != lg.GEMM_OK:
+                return None
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            call()
+            torch.cuda.synchronize()
+            one = max(time.perf_counter() - t0, 1e-5) * 1e3
+            reps = max(10, int(ms_target / one))
+            for _ in range(reps // 2):
+                call()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(reps):
+                call()
+            e1.record()
+            torch.cuda.synchronize()
+            return round(2 * M * N * K / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12, 1)
+
+        s, plan = lg.gemm_plan(0, 0, 0, 0, M, N, K, 1.0, A.data_ptr(), K, B.data_ptr(), N, 0.0, C.data_ptr(), N)
+        lg.check(s)
+        row = {"M": M, "N": N, "K": K, "planned_tile": plan.tile}
+        for tile in (5, 10, 11):
+            row[f"tile_{tile}"] = tflops(lg.GemmOpts(0, lg.GEMM_KERNEL_VALU_RING, tile, 0))
+        row["planned"] = tflops(None)
+        out.append(row)
+        del A, B, C
+    torch.cuda.empty_cache()
+    return out
+
+
 def h2d_staging_control(dev, mib: int = 256, chunk_mib: int = 4, reps: int = 3):
     """Host-to-device copy of `mib` MiB of ordinary (pageable) host memory through the
     page-locked staging ring of gemm_h2d_staged, per slot count (wall clock: the call
@@ -495,6 +549,9 @@ def main():
     ap.add_argument("--mfma-control", action="store_true",
                     help="run only the compute-bound control (matrix instructions on register operands) "
                          "and print its figures (for a counter pass of the control alone)")
+    ap.add_argument("--fp32-tiles", action="store_true",
+                    help="run only the fp32 tile-choice sweep (the planner's pick against each large "
+                         "fp32 ring tile forced, over 16 shapes) and print it")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="instead of the GEMM, run a plain device copy kernel of this many MiB "
                          "(read + write) a few times: the reference for scaling HBM counters")
@@ -524,6 +581,9 @@ def main():
     src_hash = kernel_source_hash()
     if args.mfma_control:
         print(json.dumps({"mfma_control": mfma_ceiling_control(dev), "kernel_source_hash": src_hash}), flush=True)
+        return
+    if args.fp32_tiles:
+        print(json.dumps({"fp32_tile_choice": fp32_tile_choice(dev), "kernel_source_hash": src_hash}), flush=True)
         return
 
     w = Workload(args.config, dev)

@@ -120,14 +120,17 @@ def test_plans_for_the_workloads():
     s, p = plan(F32, F32, ROW, ROW, 4096, 4096, 4096)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn, p.bk) == (128, 128, 32)
     assert p.grid == 32 * 32 and p.tile == 10 and p.threads == 256 and p.nstage == 2
-    # the round model's other picks: 3072^3 -> 128x64 (576 tiles of 128x128 would leave a
-    # second round an eighth full), 2048^3 -> one 512-thread 128x128 tile per CU, and K not a
-    # multiple of 32 -> no tile 10
+    # the round model's other picks: 3072^3 and 2048^3 -> 128x64 (576 tiles of 128x128 would
+    # leave a second round an eighth full; 256 would fill half the slots of one), 2560^3 ->
+    # 128x128 (400 tiles in one round against 800 128x64 tiles in two), and K not a multiple
+    # of 32 -> no tile 10
     assert plan(F32, F32, ROW, ROW, 3072, 3072, 3072)[1].tile == 5
-    s, p = plan(F32, F32, ROW, ROW, 2048, 2048, 2048)
+    assert plan(F32, F32, ROW, ROW, 2048, 2048, 2048)[1].tile == 5
+    assert plan(F32, F32, ROW, ROW, 2560, 2560, 2560)[1].tile == 10
+    assert plan(F32, F32, ROW, ROW, 4096, 4096, 4080)[1].tile == 5
+    # tile 11 (512 threads of 8x4) only when asked for
+    s, p = plan(F32, F32, ROW, ROW, 2048, 2048, 2048, kernel=lg.GEMM_KERNEL_VALU_RING, tile=11)
     assert s == 0 and p.tile == 11 and p.threads == 512 and p.grid == 256 and p.nstage == 4
-    assert plan(F32, F32, ROW, ROW, 4096, 4096, 4080)[1].tile == 11
-    assert plan(F32, F32, ROW, ROW, 4096, 4096, 4112)[1].tile in (5, 11)
     # fp32 256^3 NN -> direct ring, 16x16 tiles (64 of 32x32 would leave most CUs idle)
     s, p = plan(F32, F32, ROW, ROW, 256, 256, 256)
     assert s == 0 and p.kernel == lg.GEMM_KERNEL_VALU_RING and (p.bm, p.bn) == (16, 16)
@@ -502,7 +505,8 @@ def test_poison_flag_is_planned_only_where_its_variant_is_built():
         assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, nstage=S, flags=P)[0] == 0
         assert plan(F32, F32, ROW, ROW, 4096, 4096, 4096, kernel=lg.GEMM_KERNEL_VALU_RING, tile=5, nstage=S,
                     flags=P)[0] == 0
-    assert plan(F32, F32, ROW, ROW, 2048, 2048, 2048, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # tile 11
+    assert plan(F32, F32, ROW, ROW, 2048, 2048, 2048, kernel=lg.GEMM_KERNEL_VALU_RING, tile=11,
+                flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED                                          # tile 11
     assert plan(F16, F16, ROW, COL, 8192, 8192, 8192, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED   # not built for f16
     assert plan(F32, F32, ROW, ROW, 256, 256, 256, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED      # small tile 9
     assert plan(BF16, BF16, COL, COL, 512, 512, 512, flags=P)[0] == lg.GEMM_ERR_UNSUPPORTED    # staged kernel

@@ -265,15 +265,16 @@ bool ring_ok(const Problem& q, const Tile& t, bool mfma, const char** why) {
 //   ceil(tiles / resident) rounds x resident x tile area / its full-occupancy rate,
 // with the residency and rate measured on fp32 squares of 4096-8192 (NN, S at the tile's
 // default): tile 5 (128x64, 256 threads of 8x4, 3 per CU) 97.5 TFLOP/s, tile 10 (128x128,
-// 256 threads of 8x8, 2 per CU) 100.8, tile 11 (128x128, 512 threads of 8x4, 1 per CU) 88.
-// The model picks the measured best on 2048^2x2048 (11: 85 against 73 for tile 5),
-// 3072^3 (5: 86 against 69 and 65), 4096^3 (10: 102 against 92), 8192^2x4096 (10),
-// 4000x3000x2048 and 6144x2048x4096 (5, by 2-8%).  Only tiles the direct ring accepts for
+// 256 threads of 8x8, 2 per CU) 100.8.  Against both forced on 16 shapes from 2048^3 to
+// 8192^2x4096 (bench.py --fp32-tiles) the model picks the faster on 14 and loses 2-7% on
+// 6144^2x2048 and 1536x4096x4096, whose part-filled last round of 128x128 tiles costs less
+// than a full one.  (Tile 11, 128x128 with 512 threads of 8x4, one per CU, is never the
+// fastest there and stays a forced / tuner choice.)  Only tiles the direct ring accepts for
 // this problem compete (tile 10's 32-deep slabs need K % 32 == 0); tile 5 when none does.
 const Tile* valu_large_tile(const Problem& q) {
     const int64_t cus = gemm::num_compute_units();
     struct Cand { int id, per_cu; double rate; };
-    const Cand cand[] = {{5, 3, 97.5}, {10, 2, 100.8}, {11, 1, 88.0}};
+    const Cand cand[] = {{5, 3, 97.5}, {10, 2, 100.8}};
     const Tile* best = nullptr;
     double best_cost = 0.0;
     for (const Cand& c : cand) {
