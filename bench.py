@@ -9,9 +9,13 @@ HBM.  Default workload: bf16 GEMM M = N = K = 8192, A row-major and B column-maj
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--config c1..c5] [--nstage S]
                   [--no-sweep] [--no-cpu-baseline] [--full-oracle]
+  python bench.py --mfma-control | --fp32-tiles      (one measurement alone, for profiling)
 
 The other four workloads are reported under "workloads" (TFLOP/s and fraction of the
-dense peak of their arithmetic), with nStage sweeps for the pipelining comparison.  The
+dense peak of their arithmetic), with nStage sweeps for the pipelining comparison; the
+bandwidth-bound control (a pipelined copy), the compute-bound control (matrix instructions
+on register operands, with the headline's fraction of it) and host staging are reported
+beside them.  The
 headline's K timed launches run after that sweep, so that they measure the card at its
 steady (power-limited) clock rather than its ramp out of idle.  "parity" holds the
 oracle's verdict on the headline's and the f16 MLP shape's device results: a row sample
